@@ -1,0 +1,222 @@
+"""Benchmark of the calibrated-FP8 paged KV hot path on one MI355X.
+
+One step = one layer call of the full path on the 72-query / 8-KV-head layer at
+context 8,192 with a 12-token causal verify window (M=12), global attention:
+insert the 12 new BF16 K/V tokens into the FP8 cache (E4M3 with per-tensor
+scales), then paged GQA decode attention over the FP8 pages (split-KV kernel +
+cross-split combine). Steps rotate over enough distinct layer copies (different
+pools, identical contents) that the working set exceeds the 256 MB Infinity
+Cache, so KV reads come from HBM.
+
+Prints ONE JSON line. `value` is KV-read throughput of the whole step
+(algorithmic KV bytes / step time); the decode pair alone is reported as
+`roofline` (bound: HBM) with its achieved bandwidth from HIP events recorded
+on the launch stream; `cpu_baseline` times the NumPy oracle on host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--context", type=int, default=8192)
+    p.add_argument("--block-size", type=int, default=64)
+    p.add_argument("--q-len", type=int, default=12)
+    p.add_argument("--copies", type=int, default=0, help="layer copies to rotate over (0 = enough for 1 GiB)")
+    p.add_argument("--split-tiles", type=int, default=0)
+    p.add_argument("--cache-dtype", default="fp8_e4m3fn")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--ab", action="store_true", help="also time the page-size A/B and 32k context")
+    return p.parse_args()
+
+
+def algorithmic_bytes(context, q_len, hq, hkv, block_size, elem):
+    kv = context * hkv * 2 * 128 * elem          # every visible key and value once
+    q = q_len * hq * 128 * 2
+    out = q_len * hq * 128 * 4
+    meta = ((context + block_size - 1) // block_size) * 4 + 4
+    return kv, q + out + meta
+
+
+def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
+    import torch
+    from fp8_kv_paged_amd import fkv, synth
+    from fp8_kv_paged_amd.layer import PagedLayer
+
+    lay = synth.make_layer(f"c3_m{args.q_len}_{context}_p{block_size}", 1003, 0, 72, 8, block_size, args.q_len, -1,
+                           [context], cache_dtype=cache_dtype)
+    base = PagedLayer(lay, split_tiles=args.split_tiles).build()
+    kv_bytes, other = algorithmic_bytes(context, args.q_len, 72, 8, block_size, 1 if cache_dtype == "fp8_e4m3fn" else 2)
+    pool_total = 2 * base.k_pool.numel()
+    copies = args.copies or max(2, math.ceil((1 << 30) / kv_bytes))
+    layers = [base]
+    for _ in range(copies - 1):
+        c = PagedLayer(lay, poison=False, split_tiles=args.split_tiles)
+        c.k_pool.copy_(base.k_pool)
+        c.v_pool.copy_(base.v_pool)
+        c.step_k, c.step_v, c.step_slots = base.step_k, base.step_v, base.step_slots
+        layers.append(c)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    fkv.reset_counters()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            L = layers[i % copies]
+            L.insert_step(stream)
+            L.decode(stream)
+        stream.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            L = layers[(warmup + i) % copies]
+            e0, e1, e2 = ev[i]
+            e0.record(stream)
+            L.insert_step(stream)
+            e1.record(stream)
+            L.decode(stream)
+            e2.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)]
+    ins_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
+    cnt = fkv.get_counters()
+    nt = (72 // 8 * args.q_len + 15) // 16
+    assert cnt["decode_split"][0 if cache_dtype == "fp8_e4m3fn" else 1][nt - 1] == steps + warmup, cnt
+    mean = lambda xs: sum(xs) / len(xs)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    return dict(kv_bytes=kv_bytes, other_bytes=other, copies=copies, working_set=copies * kv_bytes,
+                wall_ms_per_step=wall * 1e3 / steps, step_ms=mean(step_ms), insert_ms=mean(ins_ms),
+                decode_ms=mean(dec_ms), decode_ms_median=med(dec_ms), plan_ws=base.workspace.numel(),
+                combine=cnt["decode_combine_launches"] > 0)
+
+
+def cpu_baseline(seconds):
+    """The NumPy oracle (as it stands) on the host: insert 12 tokens + paged decode of the
+    same 8k layer, repeated until about `seconds` of CPU work."""
+    import numpy as np
+    from fp8_kv_paged_amd import synth
+    from oracle import attention, paged
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lay = synth.c3_layer(8192, 64)
+    kp, vp = paged.new_pools(lay.num_blocks, 64, 8, paged.FP8)
+    L = int(lay.seq_lens[0])
+    k, v = lay.kv_bits(0, 0, L - 12)
+    paged.insert(kp, vp, k, v, lay.slots(0, 0, L - 12), lay.k_scale, lay.v_scale, 64, 8, paged.FP8)
+    ks, vs = lay.kv_bits(0, L - 12, L)
+    sl = lay.slots(0, L - 12, L)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        paged.insert(kp, vp, ks, vs, sl, lay.k_scale, lay.v_scale, 64, 8, paged.FP8)
+        attention.paged_decode(kp, vp, lay.q_bits(), lay.block_table, lay.seq_lens, 12, -1, lay.softmax_scale,
+                               lay.k_scale, lay.v_scale, 64, 8, paged.FP8)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    kv_bytes = 8192 * 8 * 256
+    return {"value": round(kv_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} oracle steps (12-token insert + paged decode, 72/8 heads, context 8192, M=12, page 64), "
+                      f"{el:.1f} s, {el / n * 1e3:.1f} ms/step"}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "fp8_kv_paged_amd", "csrc"))):
+        h.update(open(os.path.join(ROOT, "fp8_kv_paged_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(src_hash, cfg_name):
+    """HBM bytes per decode call from the committed PMC summary, if it was taken on this source."""
+    p = os.path.join(ROOT, "profiles", "decode_pmc_traffic.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != src_hash or cfg_name not in d.get("configs", {}):
+        return None
+    return d["configs"][cfg_name].get("hbm_bytes_per_call")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one MI355X: --gpus {args.gpus} is not supported (the path runs on one GPU; "
+              "see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    r = run_gpu(args, args.context, args.block_size, args.cache_dtype, args.steps, args.warmup)
+    kv = r["kv_bytes"]
+    value = kv / (r["step_ms"] * 1e-3) / 1e9
+    dec_gbs = (kv + r["other_bytes"]) / (r["decode_ms"] * 1e-3) / 1e9
+    src = source_hash()
+    cfg_name = f"c3_m{args.q_len}_{args.context}_p{args.block_size}_{args.cache_dtype}"
+    line = {
+        "metric": "decode-attn µs/layer and KV-read HBM GB/s (% of peak) at M=12, 8k ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn KV, bf16 Q, f32 accumulate" if args.cache_dtype == "fp8_e4m3fn" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"full layer, 72 Q / 8 KV heads, head 128, context {args.context}, M={args.q_len} "
+                               f"causal, global, page {args.block_size}, {args.cache_dtype} cache",
+                   "context": args.context, "q_len": args.q_len, "block_size": args.block_size,
+                   "layer_copies": r["copies"], "working_set_bytes": r["working_set"], "split_tiles": args.split_tiles},
+        "us_per_layer": round(r["step_ms"] * 1e3, 3),
+        "decode_us_per_layer": round(r["decode_ms"] * 1e3, 3),
+        "decode_us_median": round(r["decode_ms_median"] * 1e3, 3),
+        "insert_us": round(r["insert_ms"] * 1e3, 3),
+        "kv_read_pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_kv_gbs": round(kv / (r["decode_ms"] * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(src, cfg_name),
+                     "kernel": "decode_split_kernel<7,fp8> + decode_combine_kernel (one decode call)",
+                     "algorithmic_bytes": kv + r["other_bytes"]},
+        "source_hash": src,
+    }
+    if args.ab:
+        extra = {}
+        for ctx, bs in ((8192, 32), (8192, 64), (32768, 32), (32768, 64)):
+            rr = run_gpu(args, ctx, bs, "fp8_e4m3fn", max(20, args.steps // 2), 5)
+            extra[f"{ctx}_p{bs}"] = {"decode_us": round(rr["decode_ms"] * 1e3, 3),
+                                     "decode_kv_gbs": round(rr["kv_bytes"] / (rr["decode_ms"] * 1e-3) / 1e9, 1),
+                                     "insert_us": round(rr["insert_ms"] * 1e3, 3)}
+        line["ab"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,57 @@
+"""Builds libfkv.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree."""
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libfkv.so")
+OBJ_DIR = os.path.join(HERE, "_build")
+SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    # no packed fp32 instructions anywhere (the compiler would otherwise form them from float code)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # IEEE fp32 division for the quantiser
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # MFMA results in VGPR form: the accumulators of the wide row packings then spill to
+    # AGPRs only under pressure instead of bouncing through them on every rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+]
+
+
+def _compile(src):
+    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(ln for ln in (r.stderr or "").splitlines() if "packed-fp32-ops" not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    return obj, err
+
+
+def build(verbose=False):
+    """Compile every source and link libfkv.so. Always recompiles."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(_compile, SOURCES))
+    objs = [o for o, _ in results]
+    if verbose:
+        for (_, err), src in zip(results, SOURCES):
+            if err.strip():
+                print(f"[{src}]\n{err}", file=sys.stderr)
+    tmp = OUT + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

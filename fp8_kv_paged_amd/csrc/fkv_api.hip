@@ -1,0 +1,261 @@
+// C ABI of libfkv.so: argument validation, split-KV planning, launches, counters.
+// Every check runs on the host before any HIP call, so invalid calls fail without a GPU.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/fkv.h"
+#include "fkv_internal.h"
+
+namespace {
+
+constexpr int kNumCUs = 256;       // MI355X compute units
+constexpr int kMaxNT = 7;          // compiled query-row tiles: (Hq/Hkv) * q_len <= 112
+constexpr int kMaxSplitTiles = 1 << 20;
+constexpr uint64_t kAlign = 256;
+
+std::atomic<uint64_t> g_insert[2];
+std::atomic<uint64_t> g_split[2][9];
+std::atomic<uint64_t> g_combine;
+std::atomic<uint64_t> g_rejected;
+
+int reject(int code) {
+  g_rejected.fetch_add(1, std::memory_order_relaxed);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_desc(const fkv_cache_desc* d) {
+  if (!d) return FKV_EINVAL;
+  if (d->num_blocks < 1 || d->num_kv_heads < 1 || d->block_size < 1 || d->head_dim < 1) return FKV_EINVAL;
+  if (d->block_size != 32 && d->block_size != 64) return FKV_EUNSUPPORTED;
+  if (d->head_dim != FKV_HEAD_DIM) return FKV_EUNSUPPORTED;
+  if (d->cache_dtype != FKV_FP8_E4M3FN && d->cache_dtype != FKV_BF16) return FKV_EUNSUPPORTED;
+  if (d->num_kv_heads > 65535) return FKV_EUNSUPPORTED;
+  return FKV_OK;
+}
+
+int pool_bytes(const fkv_cache_desc* d, uint64_t* bytes) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  const uint64_t elem = d->cache_dtype == FKV_FP8_E4M3FN ? 1 : 2;
+  const uint64_t per_block = (uint64_t)d->num_kv_heads * (uint64_t)d->block_size * FKV_HEAD_DIM * elem;
+  if ((uint64_t)d->num_blocks > (UINT64_MAX / 4) / per_block) return FKV_EINVAL;
+  *bytes = per_block * (uint64_t)d->num_blocks;
+  return FKV_OK;
+}
+
+int check_cache(const fkv_cache* c) {
+  if (!c) return FKV_EINVAL;
+  uint64_t bytes = 0;
+  int rc = pool_bytes(&c->desc, &bytes);
+  if (rc) return rc;
+  if (!c->k_pool || !c->v_pool || c->pool_bytes != bytes) return FKV_EINVAL;
+  if (!aligned(c->k_pool, 16) || !aligned(c->v_pool, 16)) return FKV_EINVAL;
+  return FKV_OK;
+}
+
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!d) return FKV_EINVAL;
+  const int hkv = c->desc.num_kv_heads;
+  if (d->num_seqs < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 1)
+    return FKV_EINVAL;
+  if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
+  if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
+  if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
+  if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
+  if (d->q_len > FKV_MAX_Q_LEN) return FKV_EUNSUPPORTED;
+  if (d->out_dtype != FKV_OUT_F32) return FKV_EUNSUPPORTED;
+  if (d->num_seqs > 65535) return FKV_EUNSUPPORTED;
+  const int64_t group = d->num_q_heads / hkv;
+  const int64_t rows = group * d->q_len;
+  const int nt = (int)((rows + 15) / 16);
+  if (nt > kMaxNT) return FKV_EUNSUPPORTED;
+  p->nt = nt;
+  p->rows_pad = 16 * nt;
+
+  // Tiles (32 keys, aligned to absolute position) that can hold visible keys at the
+  // longest context: the whole context for global attention, window + verify rows
+  // (plus one tile of misalignment) for sliding windows.
+  const int64_t lmax = d->max_seq_len;
+  int64_t tiles_max = (lmax + 31) / 32;
+  if (d->window_left >= 0) tiles_max = std::min<int64_t>(tiles_max, ((int64_t)d->window_left + d->q_len + 31) / 32 + 1);
+  int64_t tps = d->split_tiles;
+  if (tps == 0) {
+    // Fill the chip: one 4-wave group per CU for the widest row packing, more where the
+    // register footprint allows it; each wave takes at least one tile, at most 128 per
+    // group so a long sequence still spreads over many CUs.
+    const int64_t groups_per_cu = nt <= 2 ? 4 : (nt <= 4 ? 2 : 1);
+    const int64_t waves = (int64_t)kNumCUs * groups_per_cu * fkv::kWaves;
+    const int64_t units = (int64_t)std::max(d->num_seqs, 1) * hkv * tiles_max;
+    const int64_t per_wave = std::max<int64_t>(1, (units + waves - 1) / waves);
+    tps = std::min<int64_t>(128, fkv::kWaves * per_wave);
+  }
+  const int64_t max_splits = (tiles_max + tps - 1) / tps;
+  if (max_splits > 0x7FFFFFFF) return FKV_EUNSUPPORTED;
+  p->tiles_per_split = (int)tps;
+  p->max_splits = (int)max_splits;
+  if (max_splits <= 1) {
+    p->ws_o_bytes = p->ws_ml_bytes = p->ws_bytes = 0;
+    return FKV_OK;
+  }
+  const uint64_t parts = (uint64_t)d->num_seqs * hkv * (uint64_t)max_splits;
+  p->ws_o_bytes = round_up(parts * p->rows_pad * FKV_HEAD_DIM * sizeof(float), kAlign);
+  p->ws_ml_bytes = round_up(parts * 2 * p->rows_pad * sizeof(float), kAlign);
+  p->ws_bytes = p->ws_o_bytes + p->ws_ml_bytes;
+  return FKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fkv_cache_bytes(const fkv_cache_desc* desc, size_t* k_bytes, size_t* v_bytes) {
+  if (!k_bytes || !v_bytes) return reject(FKV_EINVAL);
+  uint64_t b = 0;
+  int rc = pool_bytes(desc, &b);
+  if (rc) return reject(rc);
+  *k_bytes = (size_t)b;
+  *v_bytes = (size_t)b;
+  return FKV_OK;
+}
+
+int fkv_init_cache(const fkv_cache_desc* desc, void* k_pool, void* v_pool, fkv_cache* out) {
+  if (!out) return reject(FKV_EINVAL);
+  uint64_t b = 0;
+  int rc = pool_bytes(desc, &b);
+  if (rc) return reject(rc);
+  if (!k_pool || !v_pool || !aligned(k_pool, 16) || !aligned(v_pool, 16)) return reject(FKV_EINVAL);
+  std::memset(out, 0, sizeof(*out));
+  out->desc = *desc;
+  out->k_pool = k_pool;
+  out->v_pool = v_pool;
+  out->pool_bytes = b;
+  return FKV_OK;
+}
+
+int fkv_insert(const fkv_cache* cache, const uint16_t* k, const uint16_t* v, const int32_t* slot_mapping,
+               int32_t num_tokens, const float* k_scale, const float* v_scale, void* stream) {
+  int rc = check_cache(cache);
+  if (rc) return reject(rc);
+  if (num_tokens < 0) return reject(FKV_EINVAL);
+  if (num_tokens == 0) return FKV_OK;
+  const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
+  if (!k || !v || !slot_mapping || !aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 4))
+    return reject(FKV_EINVAL);
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))) return reject(FKV_EINVAL);
+  fkv::InsertArgs a;
+  a.k = k;
+  a.v = v;
+  a.slots = slot_mapping;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = cache->desc.num_kv_heads;
+  a.block_size = cache->desc.block_size;
+  a.num_slots = (int64_t)cache->desc.num_blocks * cache->desc.block_size;
+  if (fkv::launch_insert(a, fp8, static_cast<hipStream_t>(stream)) != hipSuccess) return reject(FKV_EHIP);
+  g_insert[fp8 ? 0 : 1].fetch_add(1, std::memory_order_relaxed);
+  return FKV_OK;
+}
+
+int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* desc, size_t* bytes) {
+  if (!bytes) return reject(FKV_EINVAL);
+  fkv::DecodePlan p;
+  int rc = plan_decode(cache, desc, &p);
+  if (rc) return reject(rc);
+  *bytes = (size_t)p.ws_bytes;
+  return FKV_OK;
+}
+
+int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                    const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                    const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  fkv::DecodePlan p;
+  int rc = plan_decode(cache, desc, &p);
+  if (rc) return reject(rc);
+  if (desc->num_seqs == 0) return FKV_OK;
+  const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
+  if (!q || !block_table || !seq_lens || !out) return reject(FKV_EINVAL);
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return reject(FKV_EINVAL);
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))) return reject(FKV_EINVAL);
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return reject(FKV_EWORKSPACE);
+  if (workspace && !aligned(workspace, 16)) return reject(FKV_EINVAL);
+
+  fkv::DecodeArgs a;
+  a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
+  a.v_pool = static_cast<const uint8_t*>(cache->v_pool);
+  a.q = q;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.out = static_cast<float*>(out);
+  a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
+  a.num_seqs = desc->num_seqs;
+  a.num_q_heads = desc->num_q_heads;
+  a.num_kv_heads = cache->desc.num_kv_heads;
+  a.group = desc->num_q_heads / cache->desc.num_kv_heads;
+  a.q_len = desc->q_len;
+  a.block_size = cache->desc.block_size;
+  a.max_blocks = desc->max_blocks_per_seq;
+  a.num_blocks = cache->desc.num_blocks;
+  a.window_left = desc->window_left;
+  a.tiles_per_split = p.tiles_per_split;
+  a.max_splits = p.max_splits;
+  a.max_seq_len = desc->max_seq_len;
+  a.rows_pad = p.rows_pad;
+  a.softmax_scale = desc->softmax_scale;
+  bool combined = false;
+  const hipError_t e = fkv::launch_decode(a, p.nt, fp8, static_cast<hipStream_t>(stream), &combined);
+  if (e == hipErrorInvalidValue) return reject(FKV_EUNSUPPORTED);
+  if (e != hipSuccess) return reject(FKV_EHIP);
+  g_split[fp8 ? 0 : 1][p.nt - 1].fetch_add(1, std::memory_order_relaxed);
+  if (combined) g_combine.fetch_add(1, std::memory_order_relaxed);
+  return FKV_OK;
+}
+
+const char* fkv_status_string(int status) {
+  switch (status) {
+    case FKV_OK: return "ok";
+    case FKV_EINVAL: return "invalid argument";
+    case FKV_EUNSUPPORTED: return "unsupported shape (no compiled kernel; no fallback)";
+    case FKV_EWORKSPACE: return "workspace missing or too small";
+    case FKV_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int fkv_get_counters(fkv_counters* out) {
+  if (!out) return FKV_EINVAL;
+  std::memset(out, 0, sizeof(*out));
+  for (int i = 0; i < 2; ++i) {
+    out->insert_launches[i] = g_insert[i].load(std::memory_order_relaxed);
+    for (int j = 0; j < 9; ++j) out->decode_split[i][j] = g_split[i][j].load(std::memory_order_relaxed);
+  }
+  out->decode_combine_launches = g_combine.load(std::memory_order_relaxed);
+  out->rejected_calls = g_rejected.load(std::memory_order_relaxed);
+  return FKV_OK;
+}
+
+int fkv_reset_counters(void) {
+  for (int i = 0; i < 2; ++i) {
+    g_insert[i].store(0);
+    for (int j = 0; j < 9; ++j) g_split[i][j].store(0);
+  }
+  g_combine.store(0);
+  g_rejected.store(0);
+  return FKV_OK;
+}
+
+}  // extern "C"

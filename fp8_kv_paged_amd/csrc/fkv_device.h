@@ -1,0 +1,88 @@
+// Device-side building blocks for gfx950: vector types, the E4M3FN encoder, fp8
+// converters, MFMA wrappers and cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fkv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+constexpr int kHeadDim = 128;
+constexpr int kTile = 32;     // keys per attention tile
+
+// ---- E4M3FN encoder --------------------------------------------------------------------
+// Round an fp32 value to the nearest E4M3FN code, ties to even, saturating to +-448 for
+// |y| >= 448 (infinities included); NaN -> 0x7F | sign. The sign of zero is kept.
+// Integer formulation: normals keep the top 3 mantissa bits after adding the
+// round-to-nearest-even bias; values below 2^-6 live on the 2^-9 subnormal grid.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // >= 448 (0x43E00000), inf included
+  if (a < 0x3C800000u) {                             // < 2^-6: multiples of 2^-9
+    const float q = __uint_as_float(a) * 512.0f;     // exact power-of-two scaling
+    return sign | (uint32_t)__builtin_rintf(q);      // RNE to an integer 0..8 (8 = 2^-6)
+  }
+  const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;  // RNE to 3 mantissa bits
+  return sign | (r - (120u << 3));                   // rebias exponent 127 -> 7
+}
+
+// ---- fp8 -> bf16 / f16 (hardware, exact for every E4M3FN code) -------------------------
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ f16x8_t fp8x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return f16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// ---- MFMA 16x16x32 ------------------------------------------------------------------------
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16] and
+// D[4*(l/16) .. +3][l%16] (row index first).
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// ---- cross-lane reductions over the four 16-lane groups ------------------------------------
+// permlane16_swap pairs lane l with l^16, permlane32_swap pairs l with l^32. Both lanes
+// of a pair receive (value of the lower lane, value of the upper lane), so the result
+// is bitwise identical on all four lanes of a column.
+__device__ __forceinline__ float group_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_f16_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+}  // namespace fkv

@@ -1,0 +1,56 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fkv {
+
+constexpr int kWaves = 4;  // waves per decode work group
+
+struct InsertArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* slots;
+  const float* k_scale;
+  const float* v_scale;
+  void* k_pool;
+  void* v_pool;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int64_t num_slots;  // num_blocks * block_size
+};
+
+// Plan of one decode call: split-KV tiling and workspace carve-up.
+struct DecodePlan {
+  int nt;              // 16-row query tiles per KV head: ceil(G*M/16)
+  int rows_pad;        // 16 * nt
+  int tiles_per_split; // 32-key tiles handled by one work group
+  int max_splits;      // grid x
+  size_t ws_o_bytes;   // fp32 partial outputs
+  size_t ws_ml_bytes;  // fp32 (m, l) per partial row
+  size_t ws_bytes;     // total, 256-byte aligned pieces
+};
+
+struct DecodeArgs {
+  const uint8_t* k_pool;
+  const uint8_t* v_pool;
+  const uint16_t* q;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const float* k_scale;
+  const float* v_scale;
+  float* out;
+  float* ws_o;
+  float* ws_ml;
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, q_len, block_size, max_blocks, num_blocks;
+  int32_t window_left, tiles_per_split, max_splits, max_seq_len, rows_pad;
+  float softmax_scale;
+};
+
+hipError_t launch_insert(const InsertArgs& a, bool fp8, hipStream_t stream);
+// Returns hipErrorInvalidValue when no kernel is compiled for (nt, fp8).
+hipError_t launch_decode(const DecodeArgs& a, int nt, bool fp8, hipStream_t stream, bool* launched_combine);
+
+}  // namespace fkv

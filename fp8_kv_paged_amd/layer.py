@@ -1,0 +1,96 @@
+"""GPU state of one attention layer driven through the C ABI.
+
+PagedLayer owns the device buffers of one layer: the two pools, the page table,
+sequence lengths, the scalar scales (kept at fixed device addresses so calls
+never synchronise) and the decode output / workspace. It uploads synthetic
+inputs from `synth.Layer` and issues insert / decode calls; all arithmetic
+happens in libfkv.so.
+"""
+
+import numpy as np
+import torch
+
+from . import fkv
+from .synth import HEAD_DIM
+
+POISON_BYTE = {"fp8_e4m3fn": 0x7F, "bf16": 0xFF}  # E4M3 NaN / BF16 NaN bit patterns
+
+
+def to_dev_bits(bits, device):
+    """uint16 BF16 bit patterns (numpy) -> a bfloat16 GPU tensor with the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class PagedLayer:
+    def __init__(self, lay, device="cuda", poison=True, split_tiles=0):
+        self.lay = lay
+        self.device = device
+        self.desc = fkv.make_cache_desc(lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.cache_dtype)
+        nbytes, _ = fkv.cache_bytes(self.desc)
+        fill = POISON_BYTE[lay.cache_dtype] if poison else 0
+        self.k_pool = torch.full((nbytes,), fill, dtype=torch.uint8, device=device)
+        self.v_pool = torch.full((nbytes,), fill, dtype=torch.uint8, device=device)
+        self.cache = fkv.init_cache(self.desc, self.k_pool, self.v_pool)
+        self.k_scale = torch.tensor([float(lay.k_scale)], dtype=torch.float32, device=device)
+        self.v_scale = torch.tensor([float(lay.v_scale)], dtype=torch.float32, device=device)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(lay.block_table)).to(device)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(lay.seq_lens)).to(device)
+        self.max_seq_len = int(max(1, lay.seq_lens.max())) if lay.num_seqs else 1
+        self.ddesc = fkv.make_decode_desc(lay.num_seqs, lay.q_len, lay.num_q_heads, lay.max_blocks, self.max_seq_len,
+                                          lay.window_left, lay.softmax_scale, split_tiles)
+        self.q = to_dev_bits(lay.q_bits(), device)
+        self.out = torch.empty((lay.num_seqs, lay.q_len, lay.num_q_heads, HEAD_DIM), dtype=torch.float32,
+                               device=device)
+        nws = fkv.decode_workspace_bytes(self.cache, self.ddesc)
+        self.workspace = torch.empty((max(nws, 16),), dtype=torch.uint8, device=device)
+        self.step_k = self.step_v = self.step_slots = None
+
+    def set_split_tiles(self, split_tiles):
+        self.ddesc.split_tiles = int(split_tiles)
+        nws = fkv.decode_workspace_bytes(self.cache, self.ddesc)
+        if nws > self.workspace.numel():
+            self.workspace = torch.empty((nws,), dtype=torch.uint8, device=self.device)
+
+    def insert_tokens(self, b, t0, t1, chunk=32768):
+        """Insert tokens [t0, t1) of sequence b (host-generated BF16) through the slot mapping."""
+        for c0 in range(t0, t1, chunk):
+            c1 = min(t1, c0 + chunk)
+            k, v = self.lay.kv_bits(b, c0, c1)
+            slots = torch.from_numpy(self.lay.slots(b, c0, c1)).to(self.device)
+            fkv.insert(self.cache, to_dev_bits(k, self.device), to_dev_bits(v, self.device), slots,
+                       self.k_scale, self.v_scale)
+
+    def prefill(self):
+        """Everything before the q_len new tokens of each sequence."""
+        for b in range(self.lay.num_seqs):
+            L = int(self.lay.seq_lens[b])
+            self.insert_tokens(b, 0, max(0, L - self.lay.q_len))
+
+    def stage_step(self):
+        """Upload the q_len new tokens of every sequence (one insert call inserts them all)."""
+        ks, vs, ss = [], [], []
+        for b in range(self.lay.num_seqs):
+            L = int(self.lay.seq_lens[b])
+            t0 = max(0, L - self.lay.q_len)
+            k, v = self.lay.kv_bits(b, t0, L)
+            ks.append(k)
+            vs.append(v)
+            ss.append(self.lay.slots(b, t0, L))
+        self.step_k = to_dev_bits(np.concatenate(ks), self.device)
+        self.step_v = to_dev_bits(np.concatenate(vs), self.device)
+        self.step_slots = torch.from_numpy(np.concatenate(ss).astype(np.int32)).to(self.device)
+
+    def insert_step(self, stream=None):
+        fkv.insert(self.cache, self.step_k, self.step_v, self.step_slots, self.k_scale, self.v_scale, stream)
+
+    def decode(self, stream=None):
+        fkv.decode_attn(self.cache, self.ddesc, self.q, self.block_table, self.seq_lens, self.k_scale, self.v_scale,
+                        self.out, self.workspace, stream)
+        return self.out
+
+    def build(self):
+        """Prefill, insert the new tokens, ready to decode."""
+        self.prefill()
+        self.stage_step()
+        self.insert_step()
+        return self

@@ -1,0 +1,205 @@
+/*
+ * fkv.h -- C ABI of libfkv.so: calibrated-FP8 paged KV cache insertion and
+ * paged GQA decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The problem statement comes from four pages of the b70-optimization-lab:
+ *   [P1] "Laguna S 2.1 INT4 -- calibrated FP8 KV on Intel B70"
+ *   [P2] "Laguna FP8 KV -- replicated embedding win, page-32 build, and host boundary"
+ *   [P3] "Laguna S 2.1 B70 campaign transfer ledger"
+ *   [P4] "Laguna S 2.1 KV-cache precision decision"
+ *
+ * Conventions shared by every call:
+ *  - Every device buffer is owned by the caller. The library allocates no
+ *    device memory, keeps no device state and never synchronises the stream.
+ *    Fixed-address buffers can therefore be refreshed in place between calls
+ *    ([P3] "Result progression": persistent fixed-address attention metadata).
+ *  - Pointers named "device" must be device-accessible and 16-byte aligned.
+ *  - Streams are hipStream_t passed as void* (NULL = the legacy default stream).
+ *    Calls are asynchronous on that stream.
+ *  - Every call returns FKV_OK or an error code. Arguments are validated on the
+ *    host before any HIP call; an unsupported shape returns FKV_EUNSUPPORTED and
+ *    never falls back to another path ([P2] "Page-32 attention experiment" and
+ *    "Transferable learnings": a fallback invalidates the result). No C++
+ *    exception crosses the ABI. The calls are thread-safe.
+ */
+#ifndef FKV_H
+#define FKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------- */
+#define FKV_OK 0
+#define FKV_EINVAL 1        /* null pointer, bad size, misalignment, inconsistent shapes     */
+#define FKV_EUNSUPPORTED 2  /* a shape no compiled kernel covers (no fallback exists)          */
+#define FKV_EWORKSPACE 3    /* workspace missing or smaller than fkv_decode_workspace_bytes   */
+#define FKV_EHIP 4          /* the HIP runtime reported an error at launch                    */
+
+/* ---- cache element types ([P1] Contract: explicit E4M3 KV; [P4] BF16 as the control) ---- */
+#define FKV_FP8_E4M3FN 1    /* OCP E4M3FN bytes: bias 7, max 448, S.1111.111 = NaN, no inf  */
+#define FKV_BF16 2          /* BF16 bit patterns, stored unchanged                            */
+
+/* ---- output types ------------------------------------------------------------------------ */
+#define FKV_OUT_F32 1
+
+#define FKV_HEAD_DIM 128
+#define FKV_MAX_Q_LEN 16
+
+/*
+ * Cache geometry. [P2] "Page-32 attention experiment": page (block) sizes 32 and
+ * 64, head size 128; [P4] "BF16 versus FP8 in concrete terms": 8 KV heads x 128.
+ *
+ * Pool layout (element = 1 byte for FP8, 2 bytes for BF16; index in elements):
+ *   K pool: index(blk, h, o, d) = ((blk*num_kv_heads + h)*block_size + o)*128 + d
+ *   V pool: index(blk, h, o, d) = (blk*num_kv_heads + h)*block_size*128
+ *                                 + (o/8)*1024 + d*8 + (o%8)
+ * for physical block blk, KV head h, offset o in the block and dimension d.
+ * Each (block, head) owns one contiguous block_size*128-element slab per pool.
+ * K rows are contiguous per key; in V every group of 8 keys is stored
+ * dimension-major, so 8 consecutive keys of one dimension are 8 consecutive
+ * elements. Key j of a sequence lives in block block_table[j / block_size] at
+ * offset j % block_size.
+ */
+typedef struct fkv_cache_desc {
+  int32_t num_blocks;    /* physical blocks in each pool, >= 1                 */
+  int32_t block_size;    /* 32 or 64                                           */
+  int32_t num_kv_heads;  /* >= 1                                               */
+  int32_t head_dim;      /* must be 128                                        */
+  int32_t cache_dtype;   /* FKV_FP8_E4M3FN or FKV_BF16                         */
+} fkv_cache_desc;
+
+/* Value handle filled by fkv_init_cache; nothing to free. */
+typedef struct fkv_cache {
+  fkv_cache_desc desc;
+  void* k_pool;          /* device */
+  void* v_pool;          /* device */
+  uint64_t pool_bytes;   /* bytes of each pool */
+} fkv_cache;
+
+/*
+ * Byte size of each pool: num_blocks * num_kv_heads * block_size * 128 * element
+ * bytes. Per token and layer that is 2 * num_kv_heads * 128 elements for K + V:
+ * 2,048 bytes in FP8 and 4,096 in BF16 at 8 KV heads ([P4] "BF16 versus FP8 in
+ * concrete terms"). Pure host arithmetic. Errors: FKV_EINVAL for a null argument,
+ * a non-positive size or an overflow; FKV_EUNSUPPORTED for block_size not in
+ * {32, 64}, head_dim != 128 or an unknown cache_dtype.
+ */
+int fkv_cache_bytes(const fkv_cache_desc* desc, size_t* k_bytes, size_t* v_bytes);
+
+/*
+ * Fills *out from desc and two caller-owned device pools of fkv_cache_bytes each.
+ * No allocation and no device work: pool contents stay undefined until tokens
+ * are inserted. Errors as fkv_cache_bytes, plus FKV_EINVAL for null or
+ * misaligned pools.
+ */
+int fkv_init_cache(const fkv_cache_desc* desc, void* k_pool, void* v_pool, fkv_cache* out);
+
+/*
+ * Cache insertion ([P1] Contract: explicit E4M3 FP8 KV with the checkpoint's
+ * calibrated scalar K/V scales, unit scales for uncalibrated draft layers, no
+ * runtime scale calculation; [P4] "What the official checkpoint requests":
+ * static, symmetric, per-tensor scales; [P1] "Initial optimization order":
+ * FP8 cache update profiled on its own).
+ *
+ *  k, v          device BF16 [num_tokens][num_kv_heads][128]
+ *  slot_mapping  device int32 [num_tokens]: token t goes to block slot/block_size,
+ *                offset slot%block_size. Negative slots, and slots >= num_blocks *
+ *                block_size, are skipped. Duplicate slots leave an undefined winner.
+ *  k_scale, v_scale  device pointers to one fp32 each (> 0, finite); read on the
+ *                device so the call needs no host sync. Ignored for a BF16 cache.
+ *
+ * FP8: each element is stored as E4M3FN(fp32(x) / fp32(scale)) with one
+ * correctly rounded fp32 division, then round-to-nearest-even to E4M3FN,
+ * saturating to +-448 for |quotient| >= 448 (infinities included); a NaN
+ * quotient stores 0x7F|sign. BF16: the bit patterns are copied.
+ * num_tokens == 0 is a no-op. Errors: FKV_EINVAL (null/misaligned pointers,
+ * num_tokens < 0), FKV_EHIP.
+ */
+int fkv_insert(const fkv_cache* cache, const uint16_t* k, const uint16_t* v, const int32_t* slot_mapping,
+               int32_t num_tokens, const float* k_scale, const float* v_scale, void* stream);
+
+/*
+ * Decode attention shape ([P1] "Initial optimization order": exact q1 and M12
+ * paged attention; [P1] Contract: width 12; [P2] "Page-32 attention experiment":
+ * q=18, kv=2, head 128, global (-1,-1) and sliding windows; [P4]: 36 layers with a
+ * 512-token window and 12 global layers).
+ */
+typedef struct fkv_decode_desc {
+  int32_t num_seqs;            /* >= 0 (0 = no-op)                                          */
+  int32_t q_len;               /* M, 1..16 query tokens per sequence (q1 = 1, M12 = 12)     */
+  int32_t num_q_heads;         /* multiple of num_kv_heads; (Hq/Hkv)*M <= 144               */
+  int32_t max_blocks_per_seq;  /* row stride of block_table, >= 1                           */
+  int32_t max_seq_len;         /* host upper bound on seq_lens[], sizes the split grid      */
+  int32_t window_left;         /* -1 = global; w >= 0: keys p-w..p visible to position p    */
+  float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
+  int32_t out_dtype;           /* FKV_OUT_F32                                               */
+  int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group   */
+} fkv_decode_desc;
+
+/*
+ * Bytes of device workspace fkv_decode_attn needs for (cache, desc): split-KV
+ * partial results. Pure host arithmetic; may be 0. Errors as fkv_decode_attn's
+ * validation.
+ */
+int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* desc, size_t* bytes);
+
+/*
+ * Paged GQA decode attention over the cache.
+ *
+ *  q            device BF16 [num_seqs][q_len][num_q_heads][128]
+ *  block_table  device int32 [num_seqs][max_blocks_per_seq], physical block ids
+ *  seq_lens     device int32 [num_seqs]: L = tokens in the cache for the sequence,
+ *               INCLUDING the q_len new tokens (already inserted on this stream);
+ *               q_len <= L <= min(max_seq_len, max_blocks_per_seq*block_size)
+ *  k_scale, v_scale  device fp32 scalars (FP8 cache; ignored for BF16)
+ *  out          device fp32 [num_seqs][q_len][num_q_heads][128]
+ *
+ * Query row i sits at position p = L - q_len + i. Key j is visible to it iff
+ * lo <= j <= p with lo = 0 (window_left = -1) or max(0, p - window_left). Query
+ * head h reads KV head h / (num_q_heads / num_kv_heads). With
+ * k = decode(byte) * k_scale and v = decode(byte) * v_scale (FP8), or the BF16
+ * values:
+ *    out[i][h] = sum_j softmax_j(softmax_scale * <q[i][h], k_j>) * v_j.
+ * The result is attention over the dequantised FP8 cache, never over the
+ * BF16 originals ([P1] Contract: exactness against an FP8 teacher).
+ * Rows with no visible key (L < q_len) are written as zeros. Values of
+ * seq_lens above the documented bound are clamped to it; block ids outside
+ * [0, num_blocks) make their 32-key tile invisible (no out-of-pool read).
+ * Reads only the cache, q, the metadata and the scales; writes only out and
+ * the workspace. The result is bitwise reproducible for a given input and
+ * split_tiles. Errors: FKV_EINVAL, FKV_EUNSUPPORTED (shape not compiled),
+ * FKV_EWORKSPACE, FKV_EHIP.
+ */
+int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                    const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                    const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* fkv_status_string(int status);
+
+/*
+ * Runtime execution proof ([P3] "Harness, recovery, and evidence lessons": a
+ * runtime entry marker or counter per experimental feature): host-side counts
+ * of kernel launches per variant since load or the last reset.
+ * decode_split[cache][nt-1] counts split kernels by cache type (0 = FP8,
+ * 1 = BF16) and query row tiles nt = ceil((Hq/Hkv)*q_len / 16).
+ */
+typedef struct fkv_counters {
+  uint64_t insert_launches[2];      /* [0] FP8, [1] BF16                       */
+  uint64_t decode_split[2][9];
+  uint64_t decode_combine_launches;
+  uint64_t rejected_calls;          /* calls that returned an error            */
+} fkv_counters;
+
+int fkv_get_counters(fkv_counters* out);
+int fkv_reset_counters(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FKV_H */

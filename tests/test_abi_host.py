@@ -1,0 +1,146 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point the
+header declares, sizes match the pages' payload figures, and invalid calls fail
+closed with the documented codes before any HIP call (no GPU needed)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from fp8_kv_paged_amd import fkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fkv.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "payload.json")))
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fkv_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 8, names
+    L = fkv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in (fkv.OK, fkv.EINVAL, fkv.EUNSUPPORTED, fkv.EWORKSPACE, fkv.EHIP):
+        assert fkv.status_string(code)
+    assert fkv.status_string(99) == "unknown status"
+
+
+def test_cache_bytes_matches_payload_pins():
+    for dt, key in (("fp8_e4m3fn", "fp8_e4m3fn"), ("bf16", "bf16")):
+        for bs in (32, 64):
+            k, v = fkv.cache_bytes(fkv.make_cache_desc(10, bs, 8, dt))
+            assert k == v
+            per_token = (k + v) // (10 * bs)
+            assert per_token == GOLD["bytes_per_token_layer"][key]
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("block_size", 16, fkv.EUNSUPPORTED), ("block_size", 128, fkv.EUNSUPPORTED), ("head_dim", 64, fkv.EUNSUPPORTED),
+    ("cache_dtype", 7, fkv.EUNSUPPORTED), ("num_blocks", 0, fkv.EINVAL), ("num_kv_heads", 0, fkv.EINVAL),
+    ("block_size", 0, fkv.EINVAL),
+])
+def test_bad_cache_desc(field, value, code):
+    d = fkv.make_cache_desc(4, 32, 2)
+    setattr(d, field, value)
+    with pytest.raises(fkv.FkvError) as e:
+        fkv.cache_bytes(d)
+    assert e.value.status == code
+
+
+def _fake_cache(num_blocks=8, bs=32, hkv=2, dt="fp8_e4m3fn"):
+    """A handle over fake aligned addresses: valid for host-only calls, never launched."""
+    d = fkv.make_cache_desc(num_blocks, bs, hkv, dt)
+    c = fkv.Cache()
+    rc = fkv.lib().fkv_init_cache(ctypes.byref(d), ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.byref(c))
+    assert rc == fkv.OK
+    return c
+
+
+def test_init_cache_rejects_null_and_misaligned_pools():
+    d = fkv.make_cache_desc(8, 32, 2)
+    c = fkv.Cache()
+    L = fkv.lib()
+    assert L.fkv_init_cache(ctypes.byref(d), None, ctypes.c_void_p(0x1000), ctypes.byref(c)) == fkv.EINVAL
+    assert L.fkv_init_cache(ctypes.byref(d), ctypes.c_void_p(0x1001), ctypes.c_void_p(0x1000), ctypes.byref(c)) == fkv.EINVAL
+    assert L.fkv_init_cache(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), None) == fkv.EINVAL
+
+
+def _ws(c, **kw):
+    args = dict(num_seqs=1, q_len=12, num_q_heads=18, max_blocks_per_seq=8, max_seq_len=256)
+    args.update(kw)
+    return fkv.decode_workspace_bytes(c, fkv.make_decode_desc(**args))
+
+
+def test_decode_validation_codes():
+    c = _fake_cache()
+    assert _ws(c) >= 0
+    bad = [
+        (dict(q_len=0), fkv.EINVAL), (dict(q_len=17), fkv.EUNSUPPORTED), (dict(num_q_heads=17), fkv.EINVAL),
+        (dict(num_q_heads=20, q_len=12), fkv.EUNSUPPORTED),  # 10 heads per KV head x 12 rows > 112
+        (dict(max_seq_len=257), fkv.EINVAL),  # beyond max_blocks_per_seq * block_size
+        (dict(max_blocks_per_seq=0), fkv.EINVAL), (dict(num_seqs=-1), fkv.EINVAL),
+        (dict(window_left=-2), fkv.EINVAL), (dict(softmax_scale=0.0), fkv.EINVAL),
+        (dict(softmax_scale=float("nan")), fkv.EINVAL), (dict(split_tiles=-1), fkv.EINVAL),
+    ]
+    for kw, code in bad:
+        with pytest.raises(fkv.FkvError) as e:
+            _ws(c, **kw)
+        assert e.value.status == code, kw
+
+
+def test_workspace_zero_for_single_split_and_sized_for_many():
+    c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
+    one = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256)
+    assert one == 0
+    many = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=8)
+    # 32 splits x 8 KV heads x 112 padded rows x (128 + 2) fp32
+    assert many >= 32 * 8 * 112 * 130 * 4
+
+
+def test_calls_fail_closed_without_touching_the_gpu():
+    L = fkv.lib()
+    c = _fake_cache()
+    d = fkv.make_decode_desc(1, 12, 18, 8, 256)
+    dev = ctypes.c_void_p(0x300000)
+    # missing workspace for a multi-split plan
+    d.split_tiles = 1
+    rc = L.fkv_decode_attn(ctypes.byref(c), ctypes.byref(d), dev, dev, dev, dev, dev, dev, None, 0, None)
+    assert rc == fkv.EWORKSPACE
+    # null q
+    rc = L.fkv_decode_attn(ctypes.byref(c), ctypes.byref(d), None, dev, dev, dev, dev, dev, dev, 1 << 30, None)
+    assert rc == fkv.EINVAL
+    # misaligned out
+    rc = L.fkv_decode_attn(ctypes.byref(c), ctypes.byref(d), dev, dev, dev, dev, dev, ctypes.c_void_p(0x300004), dev,
+                           1 << 30, None)
+    assert rc == fkv.EINVAL
+    # insert: negative count, null slots, misaligned k
+    assert L.fkv_insert(ctypes.byref(c), dev, dev, dev, -1, dev, dev, None) == fkv.EINVAL
+    assert L.fkv_insert(ctypes.byref(c), dev, dev, None, 4, dev, dev, None) == fkv.EINVAL
+    assert L.fkv_insert(ctypes.byref(c), ctypes.c_void_p(0x300002), dev, dev, 4, dev, dev, None) == fkv.EINVAL
+    # zero tokens / zero sequences are no-ops that succeed without a launch
+    assert L.fkv_insert(ctypes.byref(c), None, None, None, 0, None, None, None) == fkv.OK
+    d0 = fkv.make_decode_desc(0, 12, 18, 8, 256)
+    assert L.fkv_decode_attn(ctypes.byref(c), ctypes.byref(d0), None, None, None, None, None, None, None, 0, None) == fkv.OK
+    # a tampered handle is rejected
+    c.pool_bytes += 1
+    assert L.fkv_insert(ctypes.byref(c), dev, dev, dev, 4, dev, dev, None) == fkv.EINVAL
+
+
+def test_counters_record_rejections():
+    fkv.reset_counters()
+    c = _fake_cache()
+    with pytest.raises(fkv.FkvError):
+        _ws(c, q_len=0)
+    cnt = fkv.get_counters()
+    assert cnt["rejected_calls"] >= 1
+    assert sum(cnt["insert_launches"]) == 0

@@ -1,0 +1,180 @@
+"""GPU parity of paged decode attention against the oracle (row-normalised error
+<= 2e-3, fp32 output), on every workload and on edge cases: ragged and tiny
+contexts, windows at their boundaries, every query-row packing, poisoned
+unused slots, page-table permutation and run-to-run bitwise determinism."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_kv_paged_amd import fkv, synth
+from fp8_kv_paged_amd.layer import PagedLayer, to_dev_bits
+
+import parity
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def _check(lay, out, seqs=None, kv_heads=None, tol=parity.ATTN_TOL, label=""):
+    gpu = out.cpu().numpy()
+    worst = 0.0
+    for b in (range(lay.num_seqs) if seqs is None else seqs):
+        ref = parity.reference(lay, b, kv_heads)
+        err = parity.row_errors(gpu[b], ref)
+        worst = max(worst, float(err.max()))
+    print(f"[decode parity] {label or lay.name}: max row error {worst:.3e}", flush=True)
+    assert worst <= tol, (label or lay.name, worst)
+    return worst
+
+
+def _workloads():
+    yield "c1", synth.c1_layer
+    yield "c2", synth.c2_layer
+    yield "c3_8k_p32", lambda: synth.c3_layer(8192, 32)
+    yield "c3_8k_p64", lambda: synth.c3_layer(8192, 64)
+    yield "c3_32k_p32", lambda: synth.c3_layer(32768, 32)
+    yield "c3_32k_p64", lambda: synth.c3_layer(32768, 64)
+    yield "c4_sw_layer0", lambda: synth.c4_layer(0)
+    yield "c4_global_layer3", lambda: synth.c4_layer(3)
+    yield "c4_draft_layer48", lambda: synth.c4_layer(48)
+
+
+@pytest.mark.parametrize("name,make", list(_workloads()), ids=[n for n, _ in _workloads()])
+def test_workload_parity(name, make):
+    lay = make()
+    print(f"[decode parity] building {name}", flush=True)
+    gl = PagedLayer(lay).build()
+    fkv.reset_counters()
+    out = gl.decode()
+    torch.cuda.synchronize()
+    cnt = fkv.get_counters()
+    nt = (lay.num_q_heads // lay.num_kv_heads * lay.q_len + 15) // 16
+    assert cnt["decode_split"][0][nt - 1] == 1
+    _check(lay, out, label=name)
+
+
+@pytest.fixture(scope="module")
+def c5_fp8():
+    lay = synth.c5_layer(12)
+    print(f"[decode parity] building c5 fp8 (sum L = {int(lay.seq_lens.sum())})", flush=True)
+    return lay, PagedLayer(lay).build()
+
+
+def _c5_samples(lay):
+    order = np.argsort(lay.seq_lens)
+    return [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+
+
+@pytest.mark.parametrize("q_len", [12, 1])
+def test_c5_batched_parity_fp8(c5_fp8, q_len):
+    lay12, gl = c5_fp8
+    lay = synth.c5_layer(q_len)
+    assert np.array_equal(lay.block_table, lay12.block_table) and lay.k_scale == lay12.k_scale
+    ddesc = fkv.make_decode_desc(lay.num_seqs, q_len, 72, lay.max_blocks, int(lay.seq_lens.max()))
+    q = to_dev_bits(lay.q_bits(), "cuda")
+    out = torch.empty((lay.num_seqs, q_len, 72, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty((max(16, fkv.decode_workspace_bytes(gl.cache, ddesc)),), dtype=torch.uint8, device="cuda")
+    fkv.decode_attn(gl.cache, ddesc, q, gl.block_table, gl.seq_lens, gl.k_scale, gl.v_scale, out, ws)
+    torch.cuda.synchronize()
+    _check(lay, out, seqs=_c5_samples(lay), kv_heads=[0, 5], label=f"c5 fp8 M={q_len}")
+
+
+@pytest.mark.parametrize("q_len", [12, 1])
+def test_c5_batched_parity_bf16_cache(q_len):
+    lay = synth.c5_layer(q_len, cache_dtype="bf16", num_seqs=8)
+    print(f"[decode parity] building c5 bf16 M={q_len} (sum L = {int(lay.seq_lens.sum())})", flush=True)
+    gl = PagedLayer(lay).build()
+    out = gl.decode()
+    torch.cuda.synchronize()
+    _check(lay, out, seqs=_c5_samples(lay), kv_heads=[1, 7], label=f"c5 bf16 M={q_len}")
+
+
+EDGE = [
+    # (seq_lens, q_len, window_left, Hq, Hkv, block_size, cache_dtype)
+    ([1], 1, -1, 9, 1, 32, "fp8_e4m3fn"),
+    ([12], 12, -1, 18, 2, 64, "fp8_e4m3fn"),
+    ([12, 13, 44], 12, 0, 18, 2, 32, "fp8_e4m3fn"),
+    ([31, 32, 33, 63, 64, 65], 1, -1, 18, 2, 64, "fp8_e4m3fn"),
+    ([511, 512, 513, 523, 524, 1000], 12, 511, 18, 2, 64, "fp8_e4m3fn"),
+    ([700, 701], 5, 1, 9, 1, 32, "fp8_e4m3fn"),
+    ([333], 2, -1, 3, 1, 32, "fp8_e4m3fn"),
+    ([257, 1000], 7, -1, 16, 1, 64, "fp8_e4m3fn"),
+    ([100], 3, 17, 12, 4, 32, "fp8_e4m3fn"),
+    ([5000], 12, -1, 9, 1, 32, "fp8_e4m3fn"),
+    ([12, 77, 300], 12, 64, 18, 2, 32, "bf16"),
+    ([1, 33, 129], 1, -1, 18, 2, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"L{c[0]}-M{c[1]}-w{c[2]}-{c[3]}x{c[4]}-p{c[5]}-{c[6][:4]}" for c in EDGE])
+def test_edge_cases(case):
+    seq_lens, M, wl, hq, hkv, bs, dt = case
+    lay = synth.tiny_layer(500 + len(seq_lens) * 7 + M, seq_lens, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
+                           q_len=M, window_left=wl, cache_dtype=dt, pool_slack=2.0, outlier_rate=0.01)
+    gl = PagedLayer(lay).build()
+    out = gl.decode()
+    torch.cuda.synchronize()
+    _check(lay, out, label=str(case))
+
+
+@pytest.mark.parametrize("split_tiles", [1, 2, 3, 8, 1000])
+def test_split_granularity(split_tiles):
+    lay = synth.tiny_layer(77, [2000, 64, 900], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
+    gl = PagedLayer(lay, split_tiles=split_tiles).build()
+    out = gl.decode()
+    torch.cuda.synchronize()
+    _check(lay, out, label=f"split_tiles={split_tiles}")
+
+
+def test_page_table_permutation_is_bitwise_invariant_and_runs_are_deterministic():
+    lay = synth.tiny_layer(91, [1500, 300], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12, pool_slack=3.0)
+    a = PagedLayer(lay).build()
+    out_a = a.decode().clone()
+    out_a2 = a.decode().clone()
+    perm = np.random.default_rng(3).permutation(lay.num_blocks).astype(np.int32)
+    lay_b = synth.tiny_layer(91, [1500, 300], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12, pool_slack=3.0)
+    lay_b.block_table = perm[lay.block_table]
+    out_b = PagedLayer(lay_b).build().decode().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_a2)
+    assert torch.equal(out_a, out_b)
+    _check(lay, out_a, label="permutation")
+
+
+def test_verify_rows_match_single_query_calls():
+    """Row i of an M=12 call vs a q1 call at seq_len L-M+i+1 (reported; both gated at 2e-3)."""
+    L, M = 777, 12
+    lay = synth.tiny_layer(93, [L], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=M)
+    gl = PagedLayer(lay).build()
+    out = gl.decode().cpu().numpy()
+    worst = 0.0
+    for i in range(M):
+        d1 = fkv.make_decode_desc(1, 1, 18, lay.max_blocks, L - M + i + 1)
+        q1 = to_dev_bits(lay.q_bits()[:, i:i + 1], "cuda")
+        o1 = torch.empty((1, 1, 18, 128), dtype=torch.float32, device="cuda")
+        sl = torch.tensor([L - M + i + 1], dtype=torch.int32, device="cuda")
+        ws = torch.empty((max(16, fkv.decode_workspace_bytes(gl.cache, d1)),), dtype=torch.uint8, device="cuda")
+        fkv.decode_attn(gl.cache, d1, q1, gl.block_table, sl, gl.k_scale, gl.v_scale, o1, ws)
+        worst = max(worst, float(np.abs(o1.cpu().numpy()[0, 0] - out[0, i]).max()))
+    print(f"[decode] M12 row vs q1 call max abs difference {worst:.3e}", flush=True)
+    _check(lay, torch.from_numpy(out), label="m12 vs q1")
+
+
+def test_rows_without_visible_keys_are_zero():
+    """seq_len below q_len: rows at negative positions see nothing and are written as 0."""
+    lay = synth.tiny_layer(95, [12], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
+    gl = PagedLayer(lay).build()
+    gl.seq_lens.fill_(5)
+    out = gl.decode().cpu().numpy()
+    assert np.all(out[0, :7] == 0.0)
+    assert np.all(np.isfinite(out))
+
+
+def test_unsupported_packing_fails_closed():
+    lay = synth.tiny_layer(97, [64], num_q_heads=20, num_kv_heads=2, block_size=32, q_len=12)
+    with pytest.raises(fkv.FkvError) as e:
+        PagedLayer(lay)
+    assert e.value.status == fkv.EUNSUPPORTED
