@@ -96,9 +96,10 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
     const int64_t units = (int64_t)std::max(d->num_seqs, 1) * hkv * tiles_max;
     const int64_t per_wave = std::max<int64_t>(1, (units + waves - 1) / waves);
     tps = std::min<int64_t>(128, fkv::kWaves * per_wave);
+    tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
   }
   const int64_t max_splits = (tiles_max + tps - 1) / tps;
-  if (max_splits > 0x7FFFFFFF) return FKV_EUNSUPPORTED;
+  if (max_splits > fkv::kMaxSplits) return FKV_EUNSUPPORTED;
   p->tiles_per_split = (int)tps;
   p->max_splits = (int)max_splits;
   if (max_splits <= 1) {

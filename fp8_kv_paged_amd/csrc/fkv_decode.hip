@@ -134,6 +134,8 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, WaveState<NT>& 
   }
 
   if (!interior) {
+    // Invisible keys get -inf. The test is sign arithmetic, (j - lo) | (hi - j) < 0,
+    // turned into a bit mask, so no per-element compare masks occupy scalar registers.
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int hi = st.rpos[t];
@@ -143,7 +145,8 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, WaveState<NT>& 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = kt + 8 * q + 4 * tt + i;
-          if (j < lo || j > hi) sacc[tt][t][i] = -INFINITY;
+          const uint32_t bad = (uint32_t)(((j - lo) | (hi - j)) >> 31);
+          sacc[tt][t][i] = __uint_as_float((bad & 0xFF800000u) | (~bad & __float_as_uint(sacc[tt][t][i])));
         }
     }
     // keys outside [lo_u, L) may hold stale bytes: zero their V so 0 * NaN cannot occur
@@ -179,13 +182,16 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, WaveState<NT>& 
                            fmaxf(fmaxf(sacc[1][t][0], sacc[1][t][1]), fmaxf(sacc[1][t][2], sacc[1][t][3])));
     const float cand = group_max(mx) * C;
     const bool up = cand > st.m[t] + kLazyTau;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
-      const float alpha = up ? __builtin_amdgcn_exp2f(st.m[t] - cand) : 1.0f;
-      st.m[t] = up ? cand : st.m[t];
+    // A row's first visible keys set its reference: its accumulators are still zero,
+    // so only a raise of an existing finite reference needs the rescale.
+    const bool rescale = up && st.m[t] != -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+      const float alpha = rescale ? __builtin_amdgcn_exp2f(st.m[t] - cand) : 1.0f;
       st.lsum[t] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) st.o[t][dt] *= alpha;
     }
+    st.m[t] = up ? cand : st.m[t];
   }
 
   if constexpr (kFp8) {
@@ -439,10 +445,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
 // Merges the split partials of each (sequence, KV head) row in split order:
 // out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int kfp8) {
+// A group handles 8 rows; the (m, l) of all splits are staged in LDS first, so the
+// partial-output loads of the accumulation loop are independent of each other.
+constexpr int kCombineRows = 8;
+
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int kfp8) {
+  __shared__ float w_s[kCombineRows][kMaxSplits];
+  __shared__ float l_tot[kCombineRows];
   const int b = blockIdx.z, g = blockIdx.y;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 5);
-  const int d4 = threadIdx.x & 31;
   const int G = a.group, M = a.q_len, GM = G * M;
   const int wl = a.window_left;
   int L = a.seq_lens[b];
@@ -452,30 +462,51 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int k
   const int t_end = L > 0 ? (L + kTile - 1) / kTile : 0;
   const int ntiles = max(0, t_end - t_first);
   const int nsplit = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
-  if (nsplit <= 1 || r >= GM) return;
+  if (nsplit <= 1) return;
   const int64_t base = ((int64_t)b * a.num_kv_heads + g) * a.max_splits;
-  float mx = -INFINITY, l = 0.f;
-  f32x4_t acc{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ml = a.ws_ml + (base + s) * 2 * a.rows_pad;
-    const float ms = ml[r];
-    if (ms == -INFINITY) continue;
-    const float ls = ml[a.rows_pad + r];
-    const f32x4_t os = *reinterpret_cast<const f32x4_t*>(a.ws_o + ((base + s) * a.rows_pad + r) * kHeadDim + 4 * d4);
-    if (ms > mx) {
-      const float al = __builtin_amdgcn_exp2f(mx - ms);
-      acc *= al;
-      l *= al;
-      mx = ms;
+  const int r0 = blockIdx.x * kCombineRows;
+  const int lane = threadIdx.x & 31, rr = threadIdx.x >> 5;  // 8 rows x 32 lanes
+
+  // pass 1: row r0+rr's maximum over splits, then its weights 2^(m_s - M) and total l
+  if (r0 + rr < GM) {
+    float mx = -INFINITY;
+    for (int s2 = lane; s2 < nsplit; s2 += 32) mx = fmaxf(mx, a.ws_ml[(base + s2) * 2 * a.rows_pad + r0 + rr]);
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+    float lsum = 0.f;
+    for (int s2 = lane; s2 < nsplit; s2 += 32) {
+      const float* ml = a.ws_ml + (base + s2) * 2 * a.rows_pad;
+      const float ms = ml[r0 + rr];
+      const float wgt = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
+      w_s[rr][s2] = wgt;
+      lsum += wgt * ml[a.rows_pad + r0 + rr];
     }
-    const float wgt = __builtin_amdgcn_exp2f(ms - mx);
-    acc += os * wgt;
-    l += ls * wgt;
+    // fixed-shape butterfly: the same order for every call
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 32);
+    if (lane == 0) l_tot[rr] = lsum;
   }
+  __syncthreads();
+  const int r = r0 + rr;
+  if (r >= GM) return;
+  // pass 2: lane owns 4 dimensions; split loads are independent and unrolled
+  const float* src = a.ws_o + (base * a.rows_pad + r) * kHeadDim + 4 * lane;
+  const int64_t stride = (int64_t)a.rows_pad * kHeadDim;
+  f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+  int s2 = 0;
+  for (; s2 + 4 <= nsplit; s2 += 4) {
+    const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 0) * stride);
+    const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 1) * stride);
+    const f32x4_t o2 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 2) * stride);
+    const f32x4_t o3 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 3) * stride);
+    acc += o0 * w_s[rr][s2] + o1 * w_s[rr][s2 + 1] + o2 * w_s[rr][s2 + 2] + o3 * w_s[rr][s2 + 3];
+  }
+  for (; s2 < nsplit; ++s2) acc += *reinterpret_cast<const f32x4_t*>(src + s2 * stride) * w_s[rr][s2];
   const float vsc = kfp8 ? *a.v_scale : 1.0f;
-  const float mul = l > 0.f ? vsc / l : 0.f;
+  const float lt = l_tot[rr];
+  const float mul = lt > 0.f ? vsc / lt : 0.f;
   const int i = r / G, h = g * G + (r - i * G);
-  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4) = acc * mul;
+  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * lane) = acc * mul;
 }
 
 template <int NT, bool kFp8>
@@ -506,8 +537,8 @@ hipError_t launch_decode(const DecodeArgs& a, int nt, bool fp8, hipStream_t stre
   if (e != hipSuccess) return e;
   if (a.max_splits > 1) {
     const int rows = a.group * a.q_len;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4, a.num_kv_heads, a.num_seqs), dim3(128), 0, stream,
-                       a, fp8 ? 1 : 0);
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + kCombineRows - 1) / kCombineRows, a.num_kv_heads, a.num_seqs),
+                       dim3(256), 0, stream, a, fp8 ? 1 : 0);
     e = hipGetLastError();
     *launched_combine = true;
   }

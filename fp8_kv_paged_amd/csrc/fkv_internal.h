@@ -6,7 +6,8 @@
 
 namespace fkv {
 
-constexpr int kWaves = 4;  // waves per decode work group
+constexpr int kWaves = 4;        // waves per decode work group
+constexpr int kMaxSplits = 512;  // split-KV partials per (sequence, KV head) the combine can merge
 
 struct InsertArgs {
   const uint16_t* k;
