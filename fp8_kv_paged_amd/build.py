@@ -21,6 +21,8 @@ FLAGS = [
     # MFMA results in VGPR form: the accumulators of the wide row packings then spill to
     # AGPRs only under pressure instead of bouncing through them on every rescale
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the path produces no NaN (masks are bit operations, stale V is zeroed): max needs no NaN quieting
+    "-fno-honor-nans",
 ]
 
 

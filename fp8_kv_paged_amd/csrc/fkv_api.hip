@@ -67,6 +67,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   if (d->num_seqs < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 1)
     return FKV_EINVAL;
   if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
+  if (d->layout < 0 || d->layout > 2) return FKV_EINVAL;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
@@ -86,18 +87,20 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const int64_t lmax = d->max_seq_len;
   int64_t tiles_max = (lmax + 31) / 32;
   if (d->window_left >= 0) tiles_max = std::min<int64_t>(tiles_max, ((int64_t)d->window_left + d->q_len + 31) / 32 + 1);
+  p->layout = d->layout;
+  const fkv::SplitShapeInfo sh = fkv::split_shape(nt, d->layout);
   int64_t tps = d->split_tiles;
   if (tps == 0) {
-    // Fill the chip: one 4-wave group per CU for the widest row packing, more where the
-    // register footprint allows it; each wave takes at least one tile, at most 128 per
-    // group so a long sequence still spreads over many CUs.
-    const int64_t groups_per_cu = nt <= 2 ? 4 : (nt <= 4 ? 2 : 1);
-    const int64_t waves = (int64_t)kNumCUs * groups_per_cu * fkv::kWaves;
+    // Fill the chip: every key lane of every resident group takes at least one tile, a
+    // group at most 128 so a long sequence still spreads over many CUs.
+    const int64_t lanes = (int64_t)kNumCUs * sh.groups_per_cu * sh.k;
     const int64_t units = (int64_t)std::max(d->num_seqs, 1) * hkv * tiles_max;
-    const int64_t per_wave = std::max<int64_t>(1, (units + waves - 1) / waves);
-    tps = std::min<int64_t>(128, fkv::kWaves * per_wave);
+    const int64_t per_lane = std::max<int64_t>(1, (units + lanes - 1) / lanes);
+    tps = std::min<int64_t>(128, sh.k * per_lane);
     tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
+    if (sh.ntw <= 2) tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
   }
+  if (sh.ntw <= 2 && tps > fkv::kMaxDmaSplitTiles) return FKV_EUNSUPPORTED;
   const int64_t max_splits = (tiles_max + tps - 1) / tps;
   if (max_splits > fkv::kMaxSplits) return FKV_EUNSUPPORTED;
   p->tiles_per_split = (int)tps;
@@ -218,7 +221,8 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   a.rows_pad = p.rows_pad;
   a.softmax_scale = desc->softmax_scale;
   bool combined = false;
-  const hipError_t e = fkv::launch_decode(a, p.nt, fp8, static_cast<hipStream_t>(stream), &combined);
+  const hipError_t e = fkv::launch_decode(a, fkv::split_shape(p.nt, p.layout), fp8, static_cast<hipStream_t>(stream),
+                                          &combined);
   if (e == hipErrorInvalidValue) return reject(FKV_EUNSUPPORTED);
   if (e != hipSuccess) return reject(FKV_EHIP);
   g_split[fp8 ? 0 : 1][p.nt - 1].fetch_add(1, std::memory_order_relaxed);

@@ -8,6 +8,7 @@ namespace fkv {
 
 constexpr int kWaves = 4;        // waves per decode work group
 constexpr int kMaxSplits = 512;  // split-KV partials per (sequence, KV head) the combine can merge
+constexpr int kMaxDmaSplitTiles = 128;  // 32-key tiles per split of the LDS-pipelined kernels
 
 struct InsertArgs {
   const uint16_t* k;
@@ -26,6 +27,7 @@ struct InsertArgs {
 // Plan of one decode call: split-KV tiling and workspace carve-up.
 struct DecodePlan {
   int nt;              // 16-row query tiles per KV head: ceil(G*M/16)
+  int layout;          // work-group layout (see split_shape)
   int rows_pad;        // 16 * nt
   int tiles_per_split; // 32-key tiles handled by one work group
   int max_splits;      // grid x
@@ -51,7 +53,24 @@ struct DecodeArgs {
 };
 
 hipError_t launch_insert(const InsertArgs& a, bool fp8, hipStream_t stream);
-// Returns hipErrorInvalidValue when no kernel is compiled for (nt, fp8).
-hipError_t launch_decode(const DecodeArgs& a, int nt, bool fp8, hipStream_t stream, bool* launched_combine);
+// Work-group shape of the split kernel: R row groups of NTW row tiles each, K key lanes
+// per group (R*K waves), and how many such groups one CU holds at once.
+struct SplitShapeInfo {
+  int ntw, r, k, groups_per_cu;
+};
+
+// layout 1: row groups of at most two 16-row tiles per wave, two waves per SIMD, so one
+// wave's MFMA work overlaps another's softmax; layout 2: one group holding every row
+// tile, one wave per SIMD, each K/V byte converted once. Layout 0 picks layout 1.
+inline SplitShapeInfo split_shape(int nt, int layout) {
+  if (layout == 2 && nt >= 3) return {nt, 1, 4, 1};
+  if (nt <= 2) return {nt, 1, 4, 2};
+  if (nt <= 4) return {2, 2, 4, 1};
+  return {2, 4, 2, 1};
+}
+
+// Returns hipErrorInvalidValue when no kernel is compiled for the shape.
+hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool fp8, hipStream_t stream,
+                         bool* launched_combine);
 
 }  // namespace fkv

@@ -131,13 +131,17 @@ int fkv_insert(const fkv_cache* cache, const uint16_t* k, const uint16_t* v, con
 typedef struct fkv_decode_desc {
   int32_t num_seqs;            /* >= 0 (0 = no-op)                                          */
   int32_t q_len;               /* M, 1..16 query tokens per sequence (q1 = 1, M12 = 12)     */
-  int32_t num_q_heads;         /* multiple of num_kv_heads; (Hq/Hkv)*M <= 144               */
+  int32_t num_q_heads;         /* multiple of num_kv_heads; (Hq/Hkv)*M <= 112               */
   int32_t max_blocks_per_seq;  /* row stride of block_table, >= 1                           */
   int32_t max_seq_len;         /* host upper bound on seq_lens[], sizes the split grid      */
   int32_t window_left;         /* -1 = global; w >= 0: keys p-w..p visible to position p    */
   float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
   int32_t out_dtype;           /* FKV_OUT_F32                                               */
-  int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group   */
+  int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
+                                  (at most 128 when the work groups use layout 1)            */
+  int32_t layout;              /* work-group layout: 0 = automatic; 1 = query rows spread over
+                                  row groups of at most 32 rows per wave (two waves per SIMD);
+                                  2 = all query rows of a KV head in every wave (one per SIMD) */
 } fkv_decode_desc;
 
 /*

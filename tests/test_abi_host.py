@@ -100,8 +100,12 @@ def test_decode_validation_codes():
 
 def test_workspace_zero_for_single_split_and_sized_for_many():
     c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
-    one = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256)
+    one = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256, layout=2)
     assert one == 0
+    # row-group work groups stage at most 128 page-table entries per split
+    with pytest.raises(fkv.FkvError) as e:
+        _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256, layout=1)
+    assert e.value.status == fkv.EUNSUPPORTED
     many = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=8)
     # 32 splits x 8 KV heads x 112 padded rows x (128 + 2) fp32
     assert many >= 32 * 8 * 112 * 130 * 4

@@ -42,18 +42,19 @@ def _workloads():
     yield "c4_draft_layer48", lambda: synth.c4_layer(48)
 
 
+@pytest.mark.parametrize("layout", [1, 2])
 @pytest.mark.parametrize("name,make", list(_workloads()), ids=[n for n, _ in _workloads()])
-def test_workload_parity(name, make):
+def test_workload_parity(name, make, layout):
     lay = make()
-    print(f"[decode parity] building {name}", flush=True)
-    gl = PagedLayer(lay).build()
+    print(f"[decode parity] building {name} layout {layout}", flush=True)
+    gl = PagedLayer(lay, layout=layout).build()
     fkv.reset_counters()
     out = gl.decode()
     torch.cuda.synchronize()
     cnt = fkv.get_counters()
     nt = (lay.num_q_heads // lay.num_kv_heads * lay.q_len + 15) // 16
     assert cnt["decode_split"][0][nt - 1] == 1
-    _check(lay, out, label=name)
+    _check(lay, out, label=f"{name} layout {layout}")
 
 
 @pytest.fixture(scope="module")
@@ -109,18 +110,19 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("layout", [1, 2])
 @pytest.mark.parametrize("case", EDGE, ids=[f"L{c[0]}-M{c[1]}-w{c[2]}-{c[3]}x{c[4]}-p{c[5]}-{c[6][:4]}" for c in EDGE])
-def test_edge_cases(case):
+def test_edge_cases(case, layout):
     seq_lens, M, wl, hq, hkv, bs, dt = case
     lay = synth.tiny_layer(500 + len(seq_lens) * 7 + M, seq_lens, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
                            q_len=M, window_left=wl, cache_dtype=dt, pool_slack=2.0, outlier_rate=0.01)
-    gl = PagedLayer(lay).build()
+    gl = PagedLayer(lay, layout=layout).build()
     out = gl.decode()
     torch.cuda.synchronize()
-    _check(lay, out, label=str(case))
+    _check(lay, out, label=f"{case} layout {layout}")
 
 
-@pytest.mark.parametrize("split_tiles", [1, 2, 3, 8, 1000])
+@pytest.mark.parametrize("split_tiles", [1, 2, 3, 8, 128])
 def test_split_granularity(split_tiles):
     lay = synth.tiny_layer(77, [2000, 64, 900], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
     gl = PagedLayer(lay, split_tiles=split_tiles).build()
