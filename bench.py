@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--ab", action="store_true", help="also time the page-size A/B and 32k context")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run device-to-device copies of MIB MiB (scales the HBM byte counters)")
     return p.parse_args()
 
 
@@ -162,6 +164,19 @@ def traffic_from_profile(src_hash, cfg_name):
     return d["configs"][cfg_name].get("hbm_bytes_per_call")
 
 
+def copy_calibration(mib, steps):
+    """Plain device-to-device copies of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "copies": steps}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -170,6 +185,9 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, min(args.steps, 10)))
+        return
     r = run_gpu(args, args.context, args.block_size, args.cache_dtype, args.steps, args.warmup)
     kv = r["kv_bytes"]
     value = kv / (r["step_ms"] * 1e-3) / 1e9
