@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--q-len", type=int, default=12)
     p.add_argument("--copies", type=int, default=0, help="layer copies to rotate over (0 = enough for 1 GiB)")
     p.add_argument("--split-tiles", type=int, default=0)
+    p.add_argument("--layout", type=int, default=0, help="decode work-group layout (0 = automatic)")
     p.add_argument("--cache-dtype", default="fp8_e4m3fn")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -62,13 +63,13 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
 
     lay = synth.make_layer(f"c3_m{args.q_len}_{context}_p{block_size}", 1003, 0, 72, 8, block_size, args.q_len, -1,
                            [context], cache_dtype=cache_dtype)
-    base = PagedLayer(lay, split_tiles=args.split_tiles).build()
+    base = PagedLayer(lay, split_tiles=args.split_tiles, layout=args.layout).build()
     kv_bytes, other = algorithmic_bytes(context, args.q_len, 72, 8, block_size, 1 if cache_dtype == "fp8_e4m3fn" else 2)
     pool_total = 2 * base.k_pool.numel()
     copies = args.copies or max(2, math.ceil((1 << 30) / kv_bytes))
     layers = [base]
     for _ in range(copies - 1):
-        c = PagedLayer(lay, poison=False, split_tiles=args.split_tiles)
+        c = PagedLayer(lay, poison=False, split_tiles=args.split_tiles, layout=args.layout)
         c.k_pool.copy_(base.k_pool)
         c.v_pool.copy_(base.v_pool)
         c.step_k, c.step_v, c.step_slots = base.step_k, base.step_v, base.step_slots

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfkv.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip"]
+SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip", "fkv_rows.hip", "fkv_wide.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -26,9 +26,28 @@ FLAGS = [
 ]
 
 
+# The wide kernel keeps its NT*8 accumulators in AGPRs, the MFMA default form.
+AGPR_FORM_SOURCES = {"fkv_wide.hip"}
+
+
+def _flags(src):
+    if src not in AGPR_FORM_SOURCES:
+        return FLAGS
+    out, skip = [], False
+    for i, f in enumerate(FLAGS):
+        if skip:
+            skip = False
+            continue
+        if f == "-mllvm" and i + 1 < len(FLAGS) and FLAGS[i + 1].startswith("-amdgpu-mfma-vgpr-form"):
+            skip = True
+            continue
+        out.append(f)
+    return out
+
+
 def _compile(src):
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + _flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(ln for ln in (r.stderr or "").splitlines() if "packed-fp32-ops" not in ln)
     if r.returncode != 0:

@@ -67,7 +67,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   if (d->num_seqs < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 1)
     return FKV_EINVAL;
   if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
-  if (d->layout < 0 || d->layout > 2) return FKV_EINVAL;
+  if (d->layout < 0 || d->layout > 4) return FKV_EINVAL;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
@@ -88,9 +88,24 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   int64_t tiles_max = (lmax + 31) / 32;
   if (d->window_left >= 0) tiles_max = std::min<int64_t>(tiles_max, ((int64_t)d->window_left + d->q_len + 31) / 32 + 1);
   p->layout = d->layout;
-  const fkv::SplitShapeInfo sh = fkv::split_shape(nt, d->layout);
+  const bool fp8 = c->desc.cache_dtype == FKV_FP8_E4M3FN;
+  const fkv::SplitShapeInfo sh = fkv::split_shape(nt, d->layout, fp8);
+  p->row_groups = 1;
   int64_t tps = d->split_tiles;
-  if (tps == 0) {
+  if (sh.groups_per_cu <= 0) {
+    // row-group (0) and wide (-1) kernels: one work group per CU; row groups of a KV head
+    // multiply the work groups, the splits fill the rest of the chip
+    p->row_groups = sh.r;
+    p->rows_pad = 16 * sh.ntw * sh.r;
+    if (tps == 0) {
+      const int64_t bg = (int64_t)std::max(d->num_seqs, 1) * hkv;
+      const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * sh.r));
+      tps = (tiles_max + splits - 1) / splits;
+      tps = (tps + sh.k - 1) / sh.k * sh.k;  // whole tiles for every wave
+      tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
+      tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
+    }
+  } else if (tps == 0) {
     // Fill the chip: every key lane of every resident group takes at least one tile, a
     // group at most 128 so a long sequence still spreads over many CUs.
     const int64_t lanes = (int64_t)kNumCUs * sh.groups_per_cu * sh.k;
@@ -219,9 +234,10 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   a.max_splits = p.max_splits;
   a.max_seq_len = desc->max_seq_len;
   a.rows_pad = p.rows_pad;
+  a.row_groups = p.row_groups;
   a.softmax_scale = desc->softmax_scale;
   bool combined = false;
-  const hipError_t e = fkv::launch_decode(a, fkv::split_shape(p.nt, p.layout), fp8, static_cast<hipStream_t>(stream),
+  const hipError_t e = fkv::launch_decode(a, fkv::split_shape(p.nt, p.layout, fp8), fp8, static_cast<hipStream_t>(stream),
                                           &combined);
   if (e == hipErrorInvalidValue) return reject(FKV_EUNSUPPORTED);
   if (e != hipSuccess) return reject(FKV_EHIP);

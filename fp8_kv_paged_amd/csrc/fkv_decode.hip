@@ -926,17 +926,28 @@ static hipError_t dispatch_split(const DecodeArgs& a, const SplitShapeInfo& sh, 
   }
 }
 
+hipError_t launch_combine(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+  const int rows = a.group * a.q_len;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + kCombineRows - 1) / kCombineRows, a.num_kv_heads, a.num_seqs),
+                     dim3(256), 0, stream, a, fp8 ? 1 : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool fp8, hipStream_t stream,
                          bool* launched_combine) {
   *launched_combine = false;
   if (a.num_seqs == 0) return hipSuccess;
-  hipError_t e = fp8 ? dispatch_split<true>(a, shape, stream) : dispatch_split<false>(a, shape, stream);
+  hipError_t e;
+  if (shape.groups_per_cu == 0) {
+    e = launch_rows(a, shape.ntw, fp8, stream);
+  } else if (shape.groups_per_cu < 0) {
+    e = launch_wide(a, shape.ntw, fp8, stream);
+  } else {
+    e = fp8 ? dispatch_split<true>(a, shape, stream) : dispatch_split<false>(a, shape, stream);
+  }
   if (e != hipSuccess) return e;
   if (a.max_splits > 1) {
-    const int rows = a.group * a.q_len;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + kCombineRows - 1) / kCombineRows, a.num_kv_heads, a.num_seqs),
-                       dim3(256), 0, stream, a, fp8 ? 1 : 0);
-    e = hipGetLastError();
+    e = launch_combine(a, fp8, stream);
     *launched_combine = true;
   }
   return e;

@@ -28,7 +28,8 @@ struct InsertArgs {
 struct DecodePlan {
   int nt;              // 16-row query tiles per KV head: ceil(G*M/16)
   int layout;          // work-group layout (see split_shape)
-  int rows_pad;        // 16 * nt
+  int rows_pad;        // rows of one split partial: 16 * nt, or every row group's rows
+  int row_groups;      // work groups per (sequence, KV head, split) of the row-group kernel
   int tiles_per_split; // 32-key tiles handled by one work group
   int max_splits;      // grid x
   size_t ws_o_bytes;   // fp32 partial outputs
@@ -49,6 +50,7 @@ struct DecodeArgs {
   float* ws_ml;
   int32_t num_seqs, num_q_heads, num_kv_heads, group, q_len, block_size, max_blocks, num_blocks;
   int32_t window_left, tiles_per_split, max_splits, max_seq_len, rows_pad;
+  int32_t row_groups;  // row-group kernel: groups of 16*ntw packed rows
   float softmax_scale;
 };
 
@@ -62,12 +64,27 @@ struct SplitShapeInfo {
 // layout 1: row groups of at most two 16-row tiles per wave, two waves per SIMD, so one
 // wave's MFMA work overlaps another's softmax; layout 2: one group holding every row
 // tile, one wave per SIMD, each K/V byte converted once. Layout 0 picks layout 1.
-inline SplitShapeInfo split_shape(int nt, int layout) {
+// Layout 3: row groups of ntw tiles in separate work groups of K waves each (groups_per_cu
+// 0 marks it), one work group per CU.
+// Layout 4: every row tile in each of a work group's four waves (groups_per_cu -1 marks it).
+inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
+  if (layout == 4 && nt >= 3) return {nt, 1, 4, -1};
+  if (layout == 3) {
+    const int ntw = nt >= 2 ? 2 : 1;
+    return {ntw, (nt + ntw - 1) / ntw, fp8 ? 8 : 4, 0};
+  }
   if (layout == 2 && nt >= 3) return {nt, 1, 4, 1};
   if (nt <= 2) return {nt, 1, 4, 2};
   if (nt <= 4) return {2, 2, 4, 1};
   return {2, 4, 2, 1};
 }
+
+// Row-group split kernel (layout 3): ntw 16-row tiles per row group.
+hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
+// Wide split kernel (layout 4): nt 16-row tiles in every wave.
+hipError_t launch_wide(const DecodeArgs& a, int nt, bool fp8, hipStream_t stream);
+// Merges split partials (rows_pad rows per partial) into out.
+hipError_t launch_combine(const DecodeArgs& a, bool fp8, hipStream_t stream);
 
 // Returns hipErrorInvalidValue when no kernel is compiled for the shape.
 hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool fp8, hipStream_t stream,

@@ -141,7 +141,11 @@ typedef struct fkv_decode_desc {
                                   (at most 128 when the work groups use layout 1)            */
   int32_t layout;              /* work-group layout: 0 = automatic; 1 = query rows spread over
                                   row groups of at most 32 rows per wave (two waves per SIMD);
-                                  2 = all query rows of a KV head in every wave (one per SIMD) */
+                                  2 = all query rows of a KV head in every wave (one per SIMD);
+                                  3 = row groups of at most 32 rows in separate work groups
+                                  that share K/V tiles through the L2 of one XCD;
+                                  4 = all query rows of a KV head in each of four waves, the
+                                  output accumulators in AGPRs (3 to 7 row tiles)         */
 } fkv_decode_desc;
 
 /*

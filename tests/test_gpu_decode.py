@@ -42,7 +42,7 @@ def _workloads():
     yield "c4_draft_layer48", lambda: synth.c4_layer(48)
 
 
-@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4])
 @pytest.mark.parametrize("name,make", list(_workloads()), ids=[n for n, _ in _workloads()])
 def test_workload_parity(name, make, layout):
     lay = make()
@@ -110,7 +110,7 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("layout", [1, 2])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4])
 @pytest.mark.parametrize("case", EDGE, ids=[f"L{c[0]}-M{c[1]}-w{c[2]}-{c[3]}x{c[4]}-p{c[5]}-{c[6][:4]}" for c in EDGE])
 def test_edge_cases(case, layout):
     seq_lens, M, wl, hq, hkv, bs, dt = case
@@ -122,13 +122,14 @@ def test_edge_cases(case, layout):
     _check(lay, out, label=f"{case} layout {layout}")
 
 
+@pytest.mark.parametrize("layout", [1, 3, 4])
 @pytest.mark.parametrize("split_tiles", [1, 2, 3, 8, 128])
-def test_split_granularity(split_tiles):
+def test_split_granularity(split_tiles, layout):
     lay = synth.tiny_layer(77, [2000, 64, 900], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
-    gl = PagedLayer(lay, split_tiles=split_tiles).build()
+    gl = PagedLayer(lay, split_tiles=split_tiles, layout=layout).build()
     out = gl.decode()
     torch.cuda.synchronize()
-    _check(lay, out, label=f"split_tiles={split_tiles}")
+    _check(lay, out, label=f"split_tiles={split_tiles} layout {layout}")
 
 
 def test_page_table_permutation_is_bitwise_invariant_and_runs_are_deterministic():
