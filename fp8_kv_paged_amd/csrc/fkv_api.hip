@@ -120,6 +120,9 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   if (max_splits > fkv::kMaxSplits) return FKV_EUNSUPPORTED;
   p->tiles_per_split = (int)tps;
   p->max_splits = (int)max_splits;
+  // Row-group kernel: with at least eight (sequence, KV head) pairs, each pair's work groups
+  // go to one XCD (all eight XCDs stay busy); else each split's row groups share one.
+  p->xcd_pairs = (sh.groups_per_cu == 0 && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
   if (max_splits <= 1) {
     p->ws_o_bytes = p->ws_ml_bytes = p->ws_bytes = 0;
     return FKV_OK;
@@ -221,6 +224,7 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   a.out = static_cast<float*>(out);
   a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
+  a.xcd_pairs = p.xcd_pairs;
   a.num_seqs = desc->num_seqs;
   a.num_q_heads = desc->num_q_heads;
   a.num_kv_heads = cache->desc.num_kv_heads;

@@ -831,13 +831,14 @@ void decode_split_dma_kernel(DecodeArgs a) {
 
 // Merges the split partials of each (sequence, KV head) row in split order:
 // out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// A group handles 8 rows; the (m, l) of all splits are staged in LDS first, so the
-// partial-output loads of the accumulation loop are independent of each other.
-constexpr int kCombineRows = 8;
+// A thread owns 4 dimensions of one row; a group of 128 threads holds 4 rows. Splits are
+// taken 8 at a time: the 8 partials' (m, l) and output pieces are all requested before
+// any is used (one memory round trip per 8 splits), then folded in split order into a
+// running maximum, row sum and output (the same order for every call).
+constexpr int kCombineRows = 4;
+constexpr int kCombineChunk = 8;
 
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int kfp8) {
-  __shared__ float w_s[kCombineRows][kMaxSplits];
-  __shared__ float l_tot[kCombineRows];
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int kfp8) {
   const int b = blockIdx.z, g = blockIdx.y;
   const int G = a.group, M = a.q_len, GM = G * M;
   const int wl = a.window_left;
@@ -849,50 +850,49 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a, int k
   const int ntiles = max(0, t_end - t_first);
   const int nsplit = (ntiles + a.tiles_per_split - 1) / a.tiles_per_split;
   if (nsplit <= 1) return;
-  const int64_t base = ((int64_t)b * a.num_kv_heads + g) * a.max_splits;
-  const int r0 = blockIdx.x * kCombineRows;
-  const int lane = threadIdx.x & 31, rr = threadIdx.x >> 5;  // 8 rows x 32 lanes
-
-  // pass 1: row r0+rr's maximum over splits, then its weights 2^(m_s - M) and total l
-  if (r0 + rr < GM) {
-    float mx = -INFINITY;
-    for (int s2 = lane; s2 < nsplit; s2 += 32) mx = fmaxf(mx, a.ws_ml[(base + s2) * 2 * a.rows_pad + r0 + rr]);
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
-    float lsum = 0.f;
-    for (int s2 = lane; s2 < nsplit; s2 += 32) {
-      const float* ml = a.ws_ml + (base + s2) * 2 * a.rows_pad;
-      const float ms = ml[r0 + rr];
-      const float wgt = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
-      w_s[rr][s2] = wgt;
-      lsum += wgt * ml[a.rows_pad + r0 + rr];
-    }
-    // fixed-shape butterfly: the same order for every call
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 32);
-    if (lane == 0) l_tot[rr] = lsum;
-  }
-  __syncthreads();
-  const int r = r0 + rr;
+  const int r = blockIdx.x * kCombineRows + (threadIdx.x >> 5);
+  const int d4 = threadIdx.x & 31;
   if (r >= GM) return;
-  // pass 2: lane owns 4 dimensions; split loads are independent and unrolled
-  const float* src = a.ws_o + (base * a.rows_pad + r) * kHeadDim + 4 * lane;
-  const int64_t stride = (int64_t)a.rows_pad * kHeadDim;
+  const int64_t base = ((int64_t)b * a.num_kv_heads + g) * a.max_splits;
+  const int64_t ml_stride = 2 * (int64_t)a.rows_pad;
+  const int64_t o_stride = (int64_t)a.rows_pad * kHeadDim;
+  const float* mlp = a.ws_ml + base * ml_stride + r;
+  const float* op = a.ws_o + (base * a.rows_pad + r) * kHeadDim + 4 * d4;
+
+  float mrun = -INFINITY, lrun = 0.f;
   f32x4_t acc{0.f, 0.f, 0.f, 0.f};
-  int s2 = 0;
-  for (; s2 + 4 <= nsplit; s2 += 4) {
-    const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 0) * stride);
-    const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 1) * stride);
-    const f32x4_t o2 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 2) * stride);
-    const f32x4_t o3 = *reinterpret_cast<const f32x4_t*>(src + (s2 + 3) * stride);
-    acc += o0 * w_s[rr][s2] + o1 * w_s[rr][s2 + 1] + o2 * w_s[rr][s2 + 2] + o3 * w_s[rr][s2 + 3];
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineChunk) {
+    float ms[kCombineChunk], ls[kCombineChunk];
+    f32x4_t os[kCombineChunk];
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j) {
+      const int sj = min(s0 + j, nsplit - 1);  // clamped: in-range loads, unused past the end
+      ms[j] = mlp[sj * ml_stride];
+      ls[j] = mlp[sj * ml_stride + a.rows_pad];
+      os[j] = *reinterpret_cast<const f32x4_t*>(op + sj * o_stride);
+    }
+    float mc = mrun;
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j)
+      if (s0 + j < nsplit) mc = fmaxf(mc, ms[j]);
+    // rescale what has been folded so far to the new maximum, then fold this chunk in order
+    const float keep = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mc);
+    lrun *= keep;
+    acc *= keep;
+#pragma unroll
+    for (int j = 0; j < kCombineChunk; ++j) {
+      if (s0 + j < nsplit) {
+        const float wgt = (ms[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[j] - mc);
+        lrun += wgt * ls[j];
+        acc += os[j] * wgt;
+      }
+    }
+    mrun = mc;
   }
-  for (; s2 < nsplit; ++s2) acc += *reinterpret_cast<const f32x4_t*>(src + s2 * stride) * w_s[rr][s2];
   const float vsc = kfp8 ? *a.v_scale : 1.0f;
-  const float lt = l_tot[rr];
-  const float mul = lt > 0.f ? vsc / lt : 0.f;
+  const float mul = lrun > 0.f ? vsc / lrun : 0.f;
   const int i = r / G, h = g * G + (r - i * G);
-  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * lane) = acc * mul;
+  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4) = acc * mul;
 }
 
 template <int NTW, int R, int K, bool kFp8>
@@ -929,7 +929,7 @@ static hipError_t dispatch_split(const DecodeArgs& a, const SplitShapeInfo& sh, 
 hipError_t launch_combine(const DecodeArgs& a, bool fp8, hipStream_t stream) {
   const int rows = a.group * a.q_len;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + kCombineRows - 1) / kCombineRows, a.num_kv_heads, a.num_seqs),
-                     dim3(256), 0, stream, a, fp8 ? 1 : 0);
+                     dim3(32 * kCombineRows), 0, stream, a, fp8 ? 1 : 0);
   return hipGetLastError();
 }
 

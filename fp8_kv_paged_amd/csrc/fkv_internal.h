@@ -34,6 +34,7 @@ struct DecodePlan {
   int max_splits;      // grid x
   size_t ws_o_bytes;   // fp32 partial outputs
   size_t ws_ml_bytes;  // fp32 (m, l) per partial row
+  int xcd_pairs;       // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   size_t ws_bytes;     // total, 256-byte aligned pieces
 };
 
@@ -51,6 +52,7 @@ struct DecodeArgs {
   int32_t num_seqs, num_q_heads, num_kv_heads, group, q_len, block_size, max_blocks, num_blocks;
   int32_t window_left, tiles_per_split, max_splits, max_seq_len, rows_pad;
   int32_t row_groups;  // row-group kernel: groups of 16*ntw packed rows
+  int32_t xcd_pairs;   // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   float softmax_scale;
 };
 
@@ -63,13 +65,13 @@ struct SplitShapeInfo {
 
 // layout 1: row groups of at most two 16-row tiles per wave, two waves per SIMD, so one
 // wave's MFMA work overlaps another's softmax; layout 2: one group holding every row
-// tile, one wave per SIMD, each K/V byte converted once. Layout 0 picks layout 1.
+// tile, one wave per SIMD, each K/V byte converted once.
 // Layout 3: row groups of ntw tiles in separate work groups of K waves each (groups_per_cu
 // 0 marks it), one work group per CU.
 // Layout 4: every row tile in each of a work group's four waves (groups_per_cu -1 marks it).
 inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
   if (layout == 4 && nt >= 3) return {nt, 1, 4, -1};
-  if (layout == 3) {
+  if (layout == 3 || layout == 0) {  // layout 0 (automatic) is layout 3
     const int ntw = nt >= 2 ? 2 : 1;
     return {ntw, (nt + ntw - 1) / ntw, fp8 ? 8 : 4, 0};
   }

@@ -71,10 +71,21 @@ void decode_rows_kernel(DecodeArgs a) {
   // ---- which (sequence, KV head, split, row group): row groups of a unit share an XCD
   const int RG = a.row_groups;
   const int wg = blockIdx.x;
-  const int rg = (wg % (8 * RG)) / 8;
-  const int unit = (wg / (8 * RG)) * 8 + (wg % 8);
-  const int s = unit % a.max_splits;
-  const int bg = unit / a.max_splits;
+  int rg, s, bg;
+  if (a.xcd_pairs) {
+    // every work group of a (sequence, KV head) pair on one XCD (ids congruent mod 8): its
+    // row groups share the K/V tiles through that XCD's L2
+    const int per = a.max_splits * RG, slot = wg / 8;
+    bg = (slot / per) * 8 + (wg % 8);
+    s = (slot % per) / RG;
+    rg = (slot % per) % RG;
+  } else {
+    // the row groups of a (sequence, KV head, split) on one XCD
+    rg = (wg % (8 * RG)) / 8;
+    const int unit = (wg / (8 * RG)) * 8 + (wg % 8);
+    s = unit % a.max_splits;
+    bg = unit / a.max_splits;
+  }
   if (bg >= a.num_seqs * a.num_kv_heads) return;
   const int g = bg % a.num_kv_heads, b = bg / a.num_kv_heads;
 
@@ -451,7 +462,9 @@ void decode_rows_kernel(DecodeArgs a) {
 template <int NTW, int K, bool kFp8>
 static hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.max_splits;
-  const int64_t grid = (units + 7) / 8 * 8 * a.row_groups;
+  // per-XCD pairs: (pairs rounded up to 8) x splits x row groups; else (units rounded up to 8) x row groups
+  const int64_t grid = a.xcd_pairs ? ((int64_t)a.num_seqs * a.num_kv_heads + 7) / 8 * 8 * a.max_splits * a.row_groups
+                               : (units + 7) / 8 * 8 * a.row_groups;
   hipLaunchKernelGGL((decode_rows_kernel<NTW, K, kFp8>), dim3((unsigned)grid),
                      dim3(RowsShape<NTW, K, kFp8>::kThreads), 0, stream, a);
   return hipGetLastError();

@@ -138,8 +138,8 @@ typedef struct fkv_decode_desc {
   float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
   int32_t out_dtype;           /* FKV_OUT_F32                                               */
   int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
-                                  (at most 128 when the work groups use layout 1)            */
-  int32_t layout;              /* work-group layout: 0 = automatic; 1 = query rows spread over
+                                  (at most 128 with layouts 0, 1, 3 and 4)                  */
+  int32_t layout;              /* work-group layout: 0 = automatic (layout 3); 1 = query rows spread over
                                   row groups of at most 32 rows per wave (two waves per SIMD);
                                   2 = all query rows of a KV head in every wave (one per SIMD);
                                   3 = row groups of at most 32 rows in separate work groups
