@@ -146,6 +146,11 @@ def cpu_baseline(seconds):
                       f"{el:.1f} s, {el / n * 1e3:.1f} ms/step"}
 
 
+# split kernel each decode layout launches (layout 0, the automatic choice, is the row-group kernel)
+DECODE_KERNELS = {0: "decode_rows_kernel", 1: "decode_split_dma_kernel", 2: "decode_split_kernel",
+                  3: "decode_rows_kernel", 4: "decode_wide_kernel"}
+
+
 def source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "fp8_kv_paged_amd", "csrc"))):
@@ -220,7 +225,7 @@ def main():
         "decode_kv_gbs": round(kv / (r["decode_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(src, cfg_name),
-                     "kernel": "decode_split_kernel<7,fp8> + decode_combine_kernel (one decode call)",
+                     "kernel": f"{DECODE_KERNELS[args.layout]} + decode_combine_kernel (one decode call)",
                      "algorithmic_bytes": kv + r["other_bytes"]},
         "source_hash": src,
     }

@@ -18,36 +18,17 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE fp32 division for the quantiser
     "-fhip-fp32-correctly-rounded-divide-sqrt",
-    # MFMA results in VGPR form: the accumulators of the wide row packings then spill to
-    # AGPRs only under pressure instead of bouncing through them on every rescale
+    # builtin MFMAs in VGPR form (their results feed VALU code); accumulators that must live
+    # in AGPRs are pinned there by inline asm
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # the path produces no NaN (masks are bit operations, stale V is zeroed): max needs no NaN quieting
     "-fno-honor-nans",
 ]
 
 
-# The wide kernel keeps its NT*8 accumulators in AGPRs, the MFMA default form.
-AGPR_FORM_SOURCES = {"fkv_wide.hip"}
-
-
-def _flags(src):
-    if src not in AGPR_FORM_SOURCES:
-        return FLAGS
-    out, skip = [], False
-    for i, f in enumerate(FLAGS):
-        if skip:
-            skip = False
-            continue
-        if f == "-mllvm" and i + 1 < len(FLAGS) and FLAGS[i + 1].startswith("-amdgpu-mfma-vgpr-form"):
-            skip = True
-            continue
-        out.append(f)
-    return out
-
-
 def _compile(src):
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + _flags(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(ln for ln in (r.stderr or "").splitlines() if "packed-fp32-ops" not in ln)
     if r.returncode != 0:

@@ -78,6 +78,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const int64_t rows = group * d->q_len;
   const int nt = (int)((rows + 15) / 16);
   if (nt > kMaxNT) return FKV_EUNSUPPORTED;
+  if (d->layout == 4 && nt < 3) return FKV_EUNSUPPORTED;  // the wide kernel needs two row halves
   p->nt = nt;
   p->rows_pad = 16 * nt;
 
@@ -93,13 +94,15 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   p->row_groups = 1;
   int64_t tps = d->split_tiles;
   if (sh.groups_per_cu <= 0) {
-    // row-group (0) and wide (-1) kernels: one work group per CU; row groups of a KV head
-    // multiply the work groups, the splits fill the rest of the chip
+    // row-group (0) and wide (-1) kernels: one work group per CU; the row groups of a KV
+    // head multiply the work groups (the wide kernel keeps both row halves in one), the
+    // splits fill the rest of the chip
     p->row_groups = sh.r;
     p->rows_pad = 16 * sh.ntw * sh.r;
     if (tps == 0) {
       const int64_t bg = (int64_t)std::max(d->num_seqs, 1) * hkv;
-      const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * sh.r));
+      const int64_t wgs = sh.groups_per_cu == 0 ? sh.r : 1;  // work groups per split
+      const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * wgs));
       tps = (tiles_max + splits - 1) / splits;
       tps = (tps + sh.k - 1) / sh.k * sh.k;  // whole tiles for every wave
       tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);

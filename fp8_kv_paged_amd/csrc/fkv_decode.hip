@@ -832,11 +832,11 @@ void decode_split_dma_kernel(DecodeArgs a) {
 // Merges the split partials of each (sequence, KV head) row in split order:
 // out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // A thread owns 4 dimensions of one row; a group of 128 threads holds 4 rows. Splits are
-// taken 8 at a time: the 8 partials' (m, l) and output pieces are all requested before
-// any is used (one memory round trip per 8 splits), then folded in split order into a
+// taken 16 at a time: the 16 partials' (m, l) and output pieces are all requested before
+// any is used (one memory round trip per 16 splits), then folded in split order into a
 // running maximum, row sum and output (the same order for every call).
 constexpr int kCombineRows = 4;
-constexpr int kCombineChunk = 8;
+constexpr int kCombineChunk = 16;
 
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int kfp8) {
   const int b = blockIdx.z, g = blockIdx.y;
@@ -947,7 +947,7 @@ hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool 
   }
   if (e != hipSuccess) return e;
   if (a.max_splits > 1) {
-    e = launch_combine(a, fp8, stream);
+    e = shape.groups_per_cu < 0 ? launch_combine_lanes(a, fp8, stream) : launch_combine(a, fp8, stream);
     *launched_combine = true;
   }
   return e;

@@ -68,9 +68,11 @@ struct SplitShapeInfo {
 // tile, one wave per SIMD, each K/V byte converted once.
 // Layout 3: row groups of ntw tiles in separate work groups of K waves each (groups_per_cu
 // 0 marks it), one work group per CU.
-// Layout 4: every row tile in each of a work group's four waves (groups_per_cu -1 marks it).
+// Layout 4: one work group of four waves per (sequence, KV head, split), the rows cut into
+// two halves of ntw tiles and the keys into two lanes (groups_per_cu -1 marks it); r = 2
+// row halves, k = 2 key lanes.
 inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
-  if (layout == 4 && nt >= 3) return {nt, 1, 4, -1};
+  if (layout == 4 && nt >= 3) return {(nt + 1) / 2, 2, 2, -1};
   if (layout == 3 || layout == 0) {  // layout 0 (automatic) is layout 3
     const int ntw = nt >= 2 ? 2 : 1;
     return {ntw, (nt + ntw - 1) / ntw, fp8 ? 8 : 4, 0};
@@ -83,8 +85,10 @@ inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
 
 // Row-group split kernel (layout 3): ntw 16-row tiles per row group.
 hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
-// Wide split kernel (layout 4): nt 16-row tiles in every wave.
-hipError_t launch_wide(const DecodeArgs& a, int nt, bool fp8, hipStream_t stream);
+// Wide split kernel (layout 4): ntw 16-row tiles per row half.
+hipError_t launch_wide(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
+// Merges the wide kernel's lane-layout split partials into out.
+hipError_t launch_combine_lanes(const DecodeArgs& a, bool fp8, hipStream_t stream);
 // Merges split partials (rows_pad rows per partial) into out.
 hipError_t launch_combine(const DecodeArgs& a, bool fp8, hipStream_t stream);
 

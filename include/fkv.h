@@ -144,8 +144,10 @@ typedef struct fkv_decode_desc {
                                   2 = all query rows of a KV head in every wave (one per SIMD);
                                   3 = row groups of at most 32 rows in separate work groups
                                   that share K/V tiles through the L2 of one XCD;
-                                  4 = all query rows of a KV head in each of four waves, the
-                                  output accumulators in AGPRs (3 to 7 row tiles)         */
+                                  4 = one work group of four waves per split: two halves of
+                                  the query rows x two key lanes, one wave per SIMD, the
+                                  output accumulators in AGPRs (3 to 7 row tiles, else
+                                  FKV_EUNSUPPORTED)                                        */
 } fkv_decode_desc;
 
 /*

@@ -109,6 +109,13 @@ def test_workspace_zero_for_single_split_and_sized_for_many():
     many = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=8)
     # 32 splits x 8 KV heads x 112 padded rows x (128 + 2) fp32
     assert many >= 32 * 8 * 112 * 130 * 4
+    # layout 4: two row halves of four 16-row tiles per partial (128 rows), 32 splits per KV
+    # head at 8 KV heads; fewer than three row tiles (q1 at nine heads per KV head) is refused
+    wide = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, layout=4)
+    assert wide == 32 * 8 * 128 * 130 * 4
+    with pytest.raises(fkv.FkvError) as e:
+        _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, q_len=1, layout=4)
+    assert e.value.status == fkv.EUNSUPPORTED
 
 
 def test_calls_fail_closed_without_touching_the_gpu():

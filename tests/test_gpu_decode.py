@@ -30,6 +30,18 @@ def _check(lay, out, seqs=None, kv_heads=None, tol=parity.ATTN_TOL, label=""):
     return worst
 
 
+def _layer(lay, **kw):
+    """Built PagedLayer, or None after checking that the layout rejects the row count
+    (layout 4 keeps two halves of the query rows, so it needs at least three row tiles)."""
+    nt = (lay.num_q_heads // lay.num_kv_heads * lay.q_len + 15) // 16
+    if kw.get("layout") == 4 and nt < 3:
+        with pytest.raises(fkv.FkvError) as e:
+            PagedLayer(lay, **kw)
+        assert e.value.status == fkv.EUNSUPPORTED
+        return None
+    return PagedLayer(lay, **kw).build()
+
+
 def _workloads():
     yield "c1", synth.c1_layer
     yield "c2", synth.c2_layer
@@ -47,7 +59,9 @@ def _workloads():
 def test_workload_parity(name, make, layout):
     lay = make()
     print(f"[decode parity] building {name} layout {layout}", flush=True)
-    gl = PagedLayer(lay, layout=layout).build()
+    gl = _layer(lay, layout=layout)
+    if gl is None:
+        return
     fkv.reset_counters()
     out = gl.decode()
     torch.cuda.synchronize()
@@ -116,7 +130,9 @@ def test_edge_cases(case, layout):
     seq_lens, M, wl, hq, hkv, bs, dt = case
     lay = synth.tiny_layer(500 + len(seq_lens) * 7 + M, seq_lens, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
                            q_len=M, window_left=wl, cache_dtype=dt, pool_slack=2.0, outlier_rate=0.01)
-    gl = PagedLayer(lay, layout=layout).build()
+    gl = _layer(lay, layout=layout)
+    if gl is None:
+        return
     out = gl.decode()
     torch.cuda.synchronize()
     _check(lay, out, label=f"{case} layout {layout}")
