@@ -683,8 +683,8 @@ void decode_split_dma_kernel(DecodeArgs a) {
           "ds_read_b128 %6, %8 offset:6144\n\t"
           "ds_read_b128 %7, %8 offset:7168\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(cur.k[0][0]), "=v"(cur.k[0][1]), "=v"(cur.k[1][0]), "=v"(cur.k[1][1]), "=v"(cur.v[0]),
-            "=v"(cur.v[1]), "=v"(cur.v[2]), "=v"(cur.v[3])
+          : "=&v"(cur.k[0][0]), "=&v"(cur.k[0][1]), "=&v"(cur.k[1][0]), "=&v"(cur.k[1][1]), "=&v"(cur.v[0]),
+            "=&v"(cur.v[1]), "=&v"(cur.v[2]), "=&v"(cur.v[3])
           : "v"(addr)
           : "memory");
     } else {
@@ -698,8 +698,8 @@ void decode_split_dma_kernel(DecodeArgs a) {
           "ds_read_b128 %6, %8 offset:6144\n\t"
           "ds_read_b128 %7, %8 offset:7168\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(cur.k[0][0]), "=v"(cur.k[0][1]), "=v"(cur.k[0][2]), "=v"(cur.k[0][3]), "=v"(cur.k[1][0]),
-            "=v"(cur.k[1][1]), "=v"(cur.k[1][2]), "=v"(cur.k[1][3])
+          : "=&v"(cur.k[0][0]), "=&v"(cur.k[0][1]), "=&v"(cur.k[0][2]), "=&v"(cur.k[0][3]), "=&v"(cur.k[1][0]),
+            "=&v"(cur.k[1][1]), "=&v"(cur.k[1][2]), "=&v"(cur.k[1][3])
           : "v"(addr)
           : "memory");
       asm volatile(
@@ -712,8 +712,8 @@ void decode_split_dma_kernel(DecodeArgs a) {
           "ds_read_b128 %6, %8 offset:14336\n\t"
           "ds_read_b128 %7, %8 offset:15360\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=v"(cur.v[0]), "=v"(cur.v[1]), "=v"(cur.v[2]), "=v"(cur.v[3]), "=v"(cur.v[4]), "=v"(cur.v[5]),
-            "=v"(cur.v[6]), "=v"(cur.v[7])
+          : "=&v"(cur.v[0]), "=&v"(cur.v[1]), "=&v"(cur.v[2]), "=&v"(cur.v[3]), "=&v"(cur.v[4]), "=&v"(cur.v[5]),
+            "=&v"(cur.v[6]), "=&v"(cur.v[7])
           : "v"(addr)
           : "memory");
     }
@@ -832,11 +832,11 @@ void decode_split_dma_kernel(DecodeArgs a) {
 // Merges the split partials of each (sequence, KV head) row in split order:
 // out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // A thread owns 4 dimensions of one row; a group of 128 threads holds 4 rows. Splits are
-// taken 16 at a time: the 16 partials' (m, l) and output pieces are all requested before
-// any is used (one memory round trip per 16 splits), then folded in split order into a
+// taken 8 at a time: the 8 partials' (m, l) and output pieces are all requested before
+// any is used (one memory round trip per 8 splits), then folded in split order into a
 // running maximum, row sum and output (the same order for every call).
 constexpr int kCombineRows = 4;
-constexpr int kCombineChunk = 16;
+constexpr int kCombineChunk = 8;
 
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int kfp8) {
   const int b = blockIdx.z, g = blockIdx.y;

@@ -9,6 +9,12 @@ namespace fkv {
 
 constexpr float kLazyTau = 8.0f;  // log2 units a tile maximum may exceed the reference by
 constexpr float kLog2e = 1.4426950408889634f;
+// Reference maximum of a row that has seen no visible key: finite, so that a masked score
+// (-inf) still gives probability 0 while a visible one overflows the range check below.
+constexpr float kRefInit = -1.0e30f;
+// A lane's eight probabilities of one row tile are accepted when they sum to at most 2^15:
+// each then fits f16 (max 65504). Larger sums send the tile through the exact-maximum path.
+constexpr float kAcceptSum = 32768.f;
 
 template <bool kFp8>
 struct TileGeom {
@@ -41,7 +47,8 @@ struct TileRegs32 {
 
 // ds_read of one tile slot: lane l reads bytes 16*l of every 1 KB chunk. Inline asm so
 // that the compiler does not add a wait on every outstanding DMA before it; the caller
-// has waited for the slot's own DMAs.
+// has waited for the slot's own DMAs. The outputs are early-clobber: a later read of the
+// sequence still needs the address after an earlier one has been issued into its output.
 template <bool kFp8>
 __device__ __forceinline__ void read_slot(uint32_t addr, TileRegs32<kFp8>& r) {
   if constexpr (kFp8) {
@@ -55,8 +62,8 @@ __device__ __forceinline__ void read_slot(uint32_t addr, TileRegs32<kFp8>& r) {
         "ds_read_b128 %6, %8 offset:6144\n\t"
         "ds_read_b128 %7, %8 offset:7168\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r.k[0][0]), "=v"(r.k[0][1]), "=v"(r.k[1][0]), "=v"(r.k[1][1]), "=v"(r.v[0]), "=v"(r.v[1]),
-          "=v"(r.v[2]), "=v"(r.v[3])
+        : "=&v"(r.k[0][0]), "=&v"(r.k[0][1]), "=&v"(r.k[1][0]), "=&v"(r.k[1][1]), "=&v"(r.v[0]), "=&v"(r.v[1]),
+          "=&v"(r.v[2]), "=&v"(r.v[3])
         : "v"(addr)
         : "memory");
   } else {
@@ -70,8 +77,8 @@ __device__ __forceinline__ void read_slot(uint32_t addr, TileRegs32<kFp8>& r) {
         "ds_read_b128 %6, %8 offset:6144\n\t"
         "ds_read_b128 %7, %8 offset:7168\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r.k[0][0]), "=v"(r.k[0][1]), "=v"(r.k[0][2]), "=v"(r.k[0][3]), "=v"(r.k[1][0]),
-          "=v"(r.k[1][1]), "=v"(r.k[1][2]), "=v"(r.k[1][3])
+        : "=&v"(r.k[0][0]), "=&v"(r.k[0][1]), "=&v"(r.k[0][2]), "=&v"(r.k[0][3]), "=&v"(r.k[1][0]),
+          "=&v"(r.k[1][1]), "=&v"(r.k[1][2]), "=&v"(r.k[1][3])
         : "v"(addr)
         : "memory");
     asm volatile(
@@ -84,8 +91,8 @@ __device__ __forceinline__ void read_slot(uint32_t addr, TileRegs32<kFp8>& r) {
         "ds_read_b128 %6, %8 offset:14336\n\t"
         "ds_read_b128 %7, %8 offset:15360\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(r.v[0]), "=v"(r.v[1]), "=v"(r.v[2]), "=v"(r.v[3]), "=v"(r.v[4]), "=v"(r.v[5]), "=v"(r.v[6]),
-          "=v"(r.v[7])
+        : "=&v"(r.v[0]), "=&v"(r.v[1]), "=&v"(r.v[2]), "=&v"(r.v[3]), "=&v"(r.v[4]), "=&v"(r.v[5]), "=&v"(r.v[6]),
+          "=&v"(r.v[7])
         : "v"(addr)
         : "memory");
   }
@@ -105,6 +112,25 @@ __device__ __forceinline__ void dma_tile(const unsigned char* kb, const unsigned
   }
 #pragma unroll
   for (int j = 0; j < kHalf; ++j) __builtin_amdgcn_global_load_lds(vb + 16 * j, dst + (kHalf + j) * 1024, 16, 0, 0);
+}
+
+// O^T += V^T P^T with the accumulator held in AGPRs. The compiler keeps a register
+// array that only inline asm reads and writes in the AGPR file; left to itself it runs
+// these MFMAs in VGPR form and moves every accumulator in and out of AGPRs on each tile.
+// The asm carries the wait states its inputs need: two after a VALU write of a source
+// VGPR (the hazard recognizer does not look into inline asm).
+__device__ __forceinline__ void pv_f16(f32x4_t& acc, const f16x8_t& a, const f16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void pv_bf16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Orders every later access of one row tile's accumulators after the MFMAs in flight on
+// them (an MFMA result may be read by other instructions only 18 wait states after the
+// MFMA issues), and every later MFMA after earlier VALU writes of them.
+__device__ __forceinline__ void acc_fence(f32x4_t (&o)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
 }
 
 }  // namespace fkv
