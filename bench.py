@@ -148,7 +148,7 @@ def cpu_baseline(seconds):
 
 # split kernel each decode layout launches (layout 0, the automatic choice, is the row-group kernel)
 DECODE_KERNELS = {0: "decode_rows_kernel", 1: "decode_split_dma_kernel", 2: "decode_split_kernel",
-                  3: "decode_rows_kernel", 4: "decode_wide_kernel"}
+                  3: "decode_rows_kernel", 4: "decode_wide_kernel", 5: "decode_m32_kernel"}
 
 
 def source_hash():

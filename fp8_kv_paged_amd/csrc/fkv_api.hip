@@ -67,7 +67,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   if (d->num_seqs < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 1)
     return FKV_EINVAL;
   if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
-  if (d->layout < 0 || d->layout > 4) return FKV_EINVAL;
+  if (d->layout < 0 || d->layout > 5) return FKV_EINVAL;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
@@ -79,6 +79,8 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const int nt = (int)((rows + 15) / 16);
   if (nt > kMaxNT) return FKV_EUNSUPPORTED;
   if (d->layout == 4 && nt < 3) return FKV_EUNSUPPORTED;  // the wide kernel needs two row halves
+  const bool fp8_cache = c->desc.cache_dtype == FKV_FP8_E4M3FN;
+  if (d->layout == 5 && !fp8_cache) return FKV_EUNSUPPORTED;  // the 32-row kernel reads FP8 caches
   p->nt = nt;
   p->rows_pad = 16 * nt;
 
@@ -93,7 +95,20 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const fkv::SplitShapeInfo sh = fkv::split_shape(nt, d->layout, fp8);
   p->row_groups = 1;
   int64_t tps = d->split_tiles;
-  if (sh.groups_per_cu <= 0) {
+  if (sh.groups_per_cu == -2) {
+    // 32-row kernel: one work group per (sequence, KV head, split) holding every row; the
+    // splits fill the chip, each key lane takes whole tiles, a split at most 128 tiles
+    p->rows_pad = 32 * sh.r;
+    if (tps == 0) {
+      const int64_t bg = (int64_t)std::max(d->num_seqs, 1) * hkv;
+      const int64_t splits = std::max<int64_t>(1, kNumCUs / bg);
+      tps = (tiles_max + splits - 1) / splits;
+      tps = (tps + sh.k - 1) / sh.k * sh.k;
+      tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
+      tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
+    }
+    if (tps > fkv::kMaxDmaSplitTiles) return FKV_EUNSUPPORTED;  // the page-table window holds 128 entries
+  } else if (sh.groups_per_cu <= 0) {
     // row-group (0) and wide (-1) kernels: one work group per CU; the row groups of a KV
     // head multiply the work groups (the wide kernel keeps both row halves in one), the
     // splits fill the rest of the chip
@@ -125,7 +140,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   p->max_splits = (int)max_splits;
   // Row-group kernel: with at least eight (sequence, KV head) pairs, each pair's work groups
   // go to one XCD (all eight XCDs stay busy); else each split's row groups share one.
-  p->xcd_pairs = (sh.groups_per_cu == 0 && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
+  p->xcd_pairs = ((sh.groups_per_cu == 0 || sh.groups_per_cu == -2) && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
   if (max_splits <= 1) {
     p->ws_o_bytes = p->ws_ml_bytes = p->ws_bytes = 0;
     return FKV_OK;

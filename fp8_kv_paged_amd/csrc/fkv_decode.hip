@@ -940,6 +940,8 @@ hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool 
   hipError_t e;
   if (shape.groups_per_cu == 0) {
     e = launch_rows(a, shape.ntw, fp8, stream);
+  } else if (shape.groups_per_cu == -2) {
+    e = launch_m32(a, shape.r, fp8, stream);
   } else if (shape.groups_per_cu < 0) {
     e = launch_wide(a, shape.ntw, fp8, stream);
   } else {
@@ -947,7 +949,7 @@ hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool 
   }
   if (e != hipSuccess) return e;
   if (a.max_splits > 1) {
-    e = shape.groups_per_cu < 0 ? launch_combine_lanes(a, fp8, stream) : launch_combine(a, fp8, stream);
+    e = shape.groups_per_cu == -1 ? launch_combine_lanes(a, fp8, stream) : launch_combine(a, fp8, stream);
     *launched_combine = true;
   }
   return e;

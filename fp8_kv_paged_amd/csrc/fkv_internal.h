@@ -71,7 +71,15 @@ struct SplitShapeInfo {
 // Layout 4: one work group of four waves per (sequence, KV head, split), the rows cut into
 // two halves of ntw tiles and the keys into two lanes (groups_per_cu -1 marks it); r = 2
 // row halves, k = 2 key lanes.
+// Layout 5 (FP8 cache): one work group of eight waves per (sequence, KV head, split), the
+// rows cut into r tiles of 32 (1, 2 or 4) and the keys into k = 8 / r lanes
+// (groups_per_cu -2 marks it; ntw = r).
 inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
+  if (layout == 5) {
+    const int rows = 16 * nt;
+    const int rt = rows <= 32 ? 1 : (rows <= 64 ? 2 : 4);
+    return {rt, rt, 8 / rt, -2};
+  }
   if (layout == 4 && nt >= 3) return {(nt + 1) / 2, 2, 2, -1};
   if (layout == 3 || layout == 0) {  // layout 0 (automatic) is layout 3
     const int ntw = nt >= 2 ? 2 : 1;
@@ -85,6 +93,8 @@ inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
 
 // Row-group split kernel (layout 3): ntw 16-row tiles per row group.
 hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
+// 32-row tile kernel (layout 5): rt row tiles of 32 (1, 2 or 4), FP8 cache only.
+hipError_t launch_m32(const DecodeArgs& a, int rt, bool fp8, hipStream_t stream);
 // Wide split kernel (layout 4): ntw 16-row tiles per row half.
 hipError_t launch_wide(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
 // Merges the wide kernel's lane-layout split partials into out.

@@ -1,0 +1,499 @@
+// Paged GQA decode attention, 32-row tile kernel (layout 5).
+//
+// Operation: exact q1 / M12 paged attention over the calibrated FP8 cache ("Laguna S 2.1
+// INT4 -- calibrated FP8 KV on Intel B70", sections Contract and "Initial optimization
+// order"; 9 query heads per KV head, head 128, global and sliding windows in "Laguna FP8
+// KV -- replicated embedding win, page-32 build, and host boundary", section "Page-32
+// attention experiment").
+//
+// Work decomposition. One work group per (sequence, KV head, split) holds every packed
+// query row of the KV head (G*M rows, at most 128), so each K/V byte of the split is read
+// from memory exactly once. The rows are cut into RT tiles of 32 and the split's 32-key
+// tiles into KL key lanes: wave w computes row tile w % RT of every KL-th tile. Waves w
+// and w + 4 share a SIMD, so each SIMD holds one row tile (balanced) and two waves whose
+// MFMA and softmax phases overlap.
+//   * All waves fill an LDS ring of kDepth steps (a step = the KL tiles computed
+//     together) with global_load_lds, kDepth - 1 steps ahead; one barrier per step
+//     publishes a step and frees the slot read in the previous one. Each chunk is fetched
+//     in the order the MFMA operands want it, so the LDS reads are lane-contiguous.
+//   * S^T = K Q^T on MFMA 32x32x16 bf16 (fp8 -> bf16 exact), online softmax in the log2
+//     domain against a lazily raised per-row reference, O^T += V^T P^T on MFMA 32x32x16
+//     f16 (fp8 -> f16 exact, P rounded to f16). The S^T products of tile i+1 are issued in
+//     the same block as the probabilities of tile i, so MFMA and VALU work interleave.
+//   * After the loop the KL key lanes of a row tile merge through LDS in a fixed order
+//     and the group writes final rows (one split) or an fp32 partial (m, l, O) that
+//     decode_combine_kernel merges over splits in split order.
+//   * Work groups are numbered so that every split of one (sequence, KV head) runs on the
+//     same XCD (ids congruent mod 8) when there are at least 8 such pairs.
+//
+// Lane layout (lane l = 32 h + n). MFMA 32x32x16: A lane l holds row l%32, k = 8(l/32)+e;
+// B lane l holds column l%32, k = 8(l/32)+e; D lane l holds column l%32, rows
+// 8(v/4) + 4(l/32) + v%4 for accumulator element v.
+//   * Head dimensions are permuted the same way in Q and K: k-chunk c of lane half h is
+//     d = 32(c/2) + 16h + 8(c%2) + e, so a lane reads 16 contiguous dims per pair of chunks.
+//   * K row m of the A operand is key pi(m) (bits 2 and 3 of m swapped). Then score element
+//     v of lane (n, h) is key 16(v/8) + 8h + v%8 of query row n: elements 0..7 and 8..15 are
+//     exactly the P^T operand slices of the two 16-key halves of the PV product.
+//   * V is stored with each 8-key group dimension-major; the A operand of d-tile 2a+b,
+//     key half c' at lane (n, h) is dim 64a + 2n + b of keys 16c' + 8h + 0..7 (8 bytes), so
+//     one 16-byte read serves d-tiles 2a and 2a+1. Output element v of d-tile 2a+b at lane
+//     (n, h) is dim 64a + 16(v/4) + 8h + 2(v%4) + b of row n.
+#include "fkv_device.h"
+#include "fkv_internal.h"
+#include "fkv_tile.h"
+
+namespace fkv {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+template <int RT, int KL, bool kFp8>
+struct M32Shape {
+  static constexpr int kWaves = RT * KL;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kEs = kFp8 ? 1 : 2;
+  static constexpr int kTileBytes = 2 * kTile * kHeadDim * kEs;  // K and V of one 32-key tile
+  static constexpr int kChunks = kTileBytes / 1024;              // 1 KB DMA chunks per tile
+  static constexpr int kStepBytes = KL * kTileBytes;
+  static constexpr int kPerWave = KL * kChunks / kWaves;         // DMA instructions per wave per step
+  static constexpr int kDepth = (128 * 1024) / kStepBytes < 8 ? (128 * 1024) / kStepBytes : 8;
+  static constexpr int kRing = kDepth * kStepBytes;
+  static constexpr int kXch = kWaves * 64 * 64 * 4;              // merge exchange: 64 floats per lane per wave
+  static constexpr int kBody = kRing > kXch ? kRing : kXch;
+  static_assert(kDepth >= 2, "ring of at least two steps");
+  static_assert((kDepth - 2) * kPerWave <= 63, "vmcnt range");
+  static_assert(KL * kChunks % kWaves == 0, "DMA chunks split evenly over the waves");
+  static_assert(8 % KL == 0, "output groups split evenly over the key lanes");
+  static_assert(256 + kBody + 2 * KL * RT * 32 * 4 <= 160 * 1024, "LDS budget of one CU");
+};
+
+// O^T += V^T P^T. The accumulators stay in VGPRs (MFMA VGPR form): pinning them to AGPRs
+// would split the 256-register budget of a two-wave-per-SIMD kernel in halves.
+__device__ __forceinline__ void pv32_f16(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+// Maximum of the two lanes that hold one query row (l and l ^ 32).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Waits until at most `pending` steps of this wave's DMAs (kPer instructions each) are
+// outstanding; global_load_lds completes in issue order.
+template <int kPer, int kMaxPending>
+__device__ __forceinline__ void wait_steps(int pending) {
+  if (pending <= 0 || kMaxPending <= 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else if (pending == 1 || kMaxPending < 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPer) : "memory");
+  } else if (pending == 2 || kMaxPending < 3) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer) : "memory");
+  } else if (pending == 3 || kMaxPending < 4) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kPer) : "memory");
+  } else if (pending == 4 || kMaxPending < 5) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kPer) : "memory");
+  } else if (pending == 5 || kMaxPending < 6) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * kPer) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * kPer) : "memory");
+  }
+}
+
+__device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// K row fed by A-operand row m of a 32-key tile: bits 2 and 3 of m swapped.
+__device__ __forceinline__ int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+
+template <int RT, int KL, bool kFp8>
+__global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_m32_kernel(DecodeArgs a) {
+  typedef M32Shape<RT, KL, kFp8> S;
+  static_assert(kFp8, "the 32-row kernel reads FP8 caches");
+  constexpr int kRows = 32 * RT;
+  // (m, l) of every wave's rows, apart from the ring so that its reads never wait for DMAs
+  __shared__ float sm_ml[2 * KL * kRows];
+  // ring, then the merge exchange; 256 bytes first so that no DMA targets LDS address 0
+  __shared__ __align__(256) unsigned char lds_body[256 + S::kBody];
+  unsigned char* body = lds_body + 256;
+  float* sm_m = sm_ml;               // [kl][row]
+  float* sm_l = sm_ml + KL * kRows;  // [kl][row]
+
+  // ---- (sequence, KV head, split); with >= 8 pairs every split of a pair on one XCD
+  const int x = blockIdx.x;
+  int bg, s;
+  if (a.xcd_pairs) {
+    const int slot = x >> 3;
+    bg = (slot / a.max_splits) * 8 + (x & 7);
+    s = slot % a.max_splits;
+  } else {
+    bg = x / a.max_splits;
+    s = x % a.max_splits;
+  }
+  if (bg >= a.num_seqs * a.num_kv_heads) return;
+  const int g = bg % a.num_kv_heads, b = bg / a.num_kv_heads;
+
+  const int lane = threadIdx.x & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rt = w % RT, kl = w / RT;
+  const int G = a.group, M = a.q_len, GM = G * M;
+  const int wl = a.window_left;
+  const int bshift = a.block_size == 64 ? 1 : 0;  // 32-key tiles per page: 1 or 2
+
+  // Page-table window of the split, requested with the sequence length for global
+  // attention (the split's first tile does not depend on it).
+  const int tps = a.tiles_per_split;
+  const int32_t* btrow = a.block_table + (int64_t)b * a.max_blocks;
+  int bt_lo = 0, bt_hi = 0;
+  int lb0 = 0;
+  if (wl < 0) {
+    lb0 = (s * tps) >> bshift;
+    if (lb0 + lane < a.max_blocks) bt_lo = btrow[lb0 + lane];
+    if (lb0 + lane + 64 < a.max_blocks) bt_hi = btrow[lb0 + lane + 64];
+  }
+  int L = a.seq_lens[b];
+  L = min(L, min(a.max_seq_len, a.max_blocks * a.block_size));
+  const int lo_u = (wl < 0) ? 0 : max(0, L - M - wl);
+  const int t_first = lo_u / kTile;
+  const int t_end = L > 0 ? (L + kTile - 1) / kTile : 0;
+  const int ntiles = max(0, t_end - t_first);
+  const int nsplit = (ntiles + tps - 1) / tps;
+  if (ntiles == 0) {
+    // no visible key for any row: split 0 writes the rows as zeros
+    if (s == 0) {
+      for (int idx = threadIdx.x; idx < GM * (kHeadDim / 4); idx += S::kThreads) {
+        const int r = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+        const int i = r / G, hq = g * G + (r - i * G);
+        *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) =
+            f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
+  if (s >= nsplit) return;
+  const int tb = t_first + s * tps;
+  const int te = min(tb + tps, t_end);
+  if (wl >= 0) {
+    lb0 = tb >> bshift;
+    if (lb0 + lane < a.max_blocks) bt_lo = btrow[lb0 + lane];
+    if (lb0 + lane + 64 < a.max_blocks) bt_hi = btrow[lb0 + lane + 64];
+  }
+  const int lo_max = (wl < 0) ? 0 : max(0, L - 1 - wl);  // largest row window start
+  const int p_min = L - M;                               // smallest row position
+  float ks = *a.k_scale;
+
+  // ---- this wave's query rows and Q operand: lane (n, hh) holds dims 32j + 16hh .. +15
+  const int r = 32 * rt + n;
+  const bool row_ok = r < GM;
+  const int rpos = row_ok ? L - M + r / G : -1;
+  const bool wave_rows = 32 * rt < GM;  // wave-uniform: the row tile holds a real row
+  u32x4_t qraw[8];
+  if (row_ok) {
+    const int i = r / G, hq = g * G + (r - i * G);
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qraw[2 * j] = qp[4 * j + 2 * hh];
+      qraw[2 * j + 1] = qp[4 * j + 2 * hh + 1];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qraw[c] = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // Complete the page-table and Q loads through an asm that redefines their registers:
+  // later reads carry no load dependence, so the compiler adds no wait on the DMAs below,
+  // whose counts the loop relies on.
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]), "+v"(qraw[4]),
+                 "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7])::"memory");
+  const float C = a.softmax_scale * ks * kLog2e;
+  auto block_of = [&](int tile) -> int {
+    const int e = (tile >> bshift) - lb0;
+    return __builtin_amdgcn_readlane(e < 64 ? bt_lo : bt_hi, e & 63);
+  };
+
+  // ---- this wave's DMA chunks: kPerWave fixed (key lane, chunk) pairs per step
+  const int nsteps = (te - tb + KL - 1) / KL;
+  const int64_t slab_bytes = (int64_t)a.block_size * kHeadDim;
+  uint32_t src_off[S::kPerWave];
+  int dma_tl[S::kPerWave];
+  const unsigned char* dma_pool[S::kPerWave];
+  uint32_t dma_lds[S::kPerWave];
+#pragma unroll
+  for (int u = 0; u < S::kPerWave; ++u) {
+    const int qq = w * S::kPerWave + u;
+    const int tl = qq / S::kChunks, j = qq % S::kChunks;
+    dma_tl[u] = tl;
+    dma_pool[u] = j >= 4 ? a.v_pool : a.k_pool;
+    dma_lds[u] = (uint32_t)(tl * S::kTileBytes + j * 1024);
+    if (j < 4) {
+      src_off[u] = (uint32_t)(key_of_row(n) * kHeadDim + 32 * j + 16 * hh);
+    } else {
+      const int cp = (j - 4) >> 1, aa = (j - 4) & 1;
+      src_off[u] = (uint32_t)((2 * cp + hh) * 1024 + 512 * aa + 16 * n);
+    }
+  }
+  auto issue = [&](int i) {
+    unsigned char* slot = body + (i % S::kDepth) * S::kStepBytes;
+#pragma unroll
+    for (int u = 0; u < S::kPerWave; ++u) {
+      // a tile past the split's end re-fetches its last tile (same instruction count per step)
+      const int tile = min(tb + KL * i + dma_tl[u], te - 1);
+      int blk = block_of(tile);
+      blk = ((unsigned)blk < (unsigned)a.num_blocks) ? blk : 0;
+      const int64_t off = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes + (int64_t)(tile & bshift) * (kTile * kHeadDim);
+      const unsigned char* src = dma_pool[u] + off + src_off[u];
+      // explicit void pointers: the host pass otherwise drops the kernel's launch stub
+      __builtin_amdgcn_global_load_lds((const void*)src, (void*)(slot + dma_lds[u]), 16, 0, 0);
+    }
+  };
+  const uint32_t ring_lane = (uint32_t)(uintptr_t)body + (uint32_t)(kl * S::kTileBytes) + 16u * (uint32_t)lane;
+
+  // ---- online-softmax state of the lane's row
+  f32x16_t o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+  float m_ref = kRefInit, lsum = 0.f;
+
+  // ---- S^T = K Q^T of one tile (fp8 -> bf16 conversions feed the MFMAs one chunk at a time)
+  auto qk = [&](const TileRegs32<true>& x, f32x16_t& sc) {
+    const u32x4_t kraw[4] = {x.k[0][0], x.k[0][1], x.k[1][0], x.k[1][1]};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4_t& kr = kraw[c >> 1];
+      const bf16x8_t kf = fp8x8_to_bf16x8(kr[(c & 1) * 2], kr[(c & 1) * 2 + 1]);
+      sc = mfma32_bf16(kf, __builtin_bit_cast(bf16x8_t, qraw[c]), sc);
+    }
+  };
+  // ---- masking of a tile that is not visible to every row of the KV head: invisible
+  // scores become -inf; keys outside [lo_u, L), and every key of an invalid block, may hold
+  // stale bytes, so their V bytes are zeroed (0 * NaN cannot occur)
+  auto mask = [&](int tile, f32x16_t& sc, TileRegs32<true>& x) {
+    const int kt = tile * kTile;
+    const bool valid = (unsigned)block_of(tile) < (unsigned)a.num_blocks;
+    const int hi = valid ? rpos : -1;
+    const int lo = (wl < 0) ? 0 : max(0, rpos - wl);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = kt + 16 * (v >> 3) + 8 * hh + (v & 7);
+      const uint32_t bad = (uint32_t)(((j - lo) | (hi - j)) >> 31);
+      sc[v] = __uint_as_float((bad & 0xFF800000u) | (~bad & __float_as_uint(sc[v])));
+    }
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp) {
+      const int k0 = kt + 16 * cp + 8 * hh;
+      const int e0 = valid ? min(8, max(0, lo_u - k0)) : 8;
+      const int e1 = min(8, max(0, L - k0));
+      if (e0 > 0 || e1 < 8) {
+        const uint64_t keep =
+            (e1 >= 8 ? ~0ull : ((1ull << (8 * e1)) - 1)) & (e0 >= 8 ? 0ull : ~((1ull << (8 * e0)) - 1));
+        const uint32_t klo = (uint32_t)keep, khi = (uint32_t)(keep >> 32);
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          x.v[2 * cp + aa][0] &= klo;
+          x.v[2 * cp + aa][1] &= khi;
+          x.v[2 * cp + aa][2] &= klo;
+          x.v[2 * cp + aa][3] &= khi;
+        }
+      }
+    }
+  };
+  auto interior = [&](int tile) -> bool {
+    const int kt = tile * kTile;
+    return ((unsigned)block_of(tile) < (unsigned)a.num_blocks) && (kt >= lo_max) && (kt + kTile - 1 <= p_min);
+  };
+  // ---- probabilities against the current reference; the lane's sum is the range check
+  auto probs = [&](const f32x16_t& sc, uint32_t (&hw)[8]) -> float {
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(sc[v], C, -m_ref));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) hw[k] = pack_f16_rtz(p[2 * k], p[2 * k + 1]);
+    // the row sum uses the same rounded probabilities the PV product sees
+    const f16x2_t one2 = __builtin_bit_cast(f16x2_t, 0x3C003C00u);
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[k]), one2, l, false);
+    return l;
+  };
+  // cold path: exact row maximum; raise the reference of rows exceeded by more than
+  // kLazyTau, rescale those rows, recompute the probabilities
+  auto raise = [&](const f32x16_t& sc, uint32_t (&hw)[8], float& lt) {
+    float mx = sc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    const float cand = pair_max(mx) * C;  // -inf when the row sees no key of this tile
+    const bool up = cand > m_ref + kLazyTau;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - cand) : 1.0f;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      m_ref = up ? cand : m_ref;
+      lt = probs(sc, hw);
+    }
+  };
+  // ---- O^T += V^T P^T: d-tile 2a+b, key half c' reads bytes 8b..8b+7 of V chunk (c', a)
+  auto pv = [&](const TileRegs32<true>& x, const uint32_t (&hw)[8]) {
+    const f16x8_t P0 = __builtin_bit_cast(f16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
+    const f16x8_t P1 = __builtin_bit_cast(f16x8_t, u32x4_t{hw[4], hw[5], hw[6], hw[7]});
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const u32x4_t& v0 = x.v[aa];
+        const u32x4_t& v1 = x.v[2 + aa];
+        pv32_f16(o[2 * aa + bb], fp8x8_to_f16x8(v0[2 * bb], v0[2 * bb + 1]), P0);
+        pv32_f16(o[2 * aa + bb], fp8x8_to_f16x8(v1[2 * bb], v1[2 * bb + 1]), P1);
+      }
+  };
+
+  // ---- the pipeline. kDepth steps are in flight; one barrier per step publishes a step
+  // and certifies that every wave has read the slot the next request overwrites. A wave
+  // computes S^T of tile i+1 in the same block as the probabilities of tile i, so MFMA and
+  // VALU work interleave, then O^T += V^T P^T of tile i.
+  const int nfull = wave_rows ? (te - tb - kl + KL - 1) / KL : 0;  // this wave's tiles
+  const uint32_t slot0 = ring_lane;
+#pragma unroll
+  for (int p = 0; p < S::kDepth - 1; ++p)
+    if (p < nsteps) issue(p);
+  wait_steps<S::kPerWave, S::kDepth - 2>(min(nsteps - 1, S::kDepth - 2));
+  asm volatile("s_barrier" ::: "memory");
+  if (S::kDepth - 1 < nsteps) issue(S::kDepth - 1);
+  TileRegs32<true> xa, xb;
+  f32x16_t sa, sb;
+  if (nfull > 0) {
+    read_slot<true>(slot0, xa);
+    qk(xa, sa);
+  }
+  for (int i = 0; i < nsteps; ++i) {
+    if (i + 1 < nsteps) {
+      wait_steps<S::kPerWave, S::kDepth - 2>(min(nsteps - 2 - i, S::kDepth - 2));
+      asm volatile("s_barrier" ::: "memory");
+      if (i + S::kDepth < nsteps) issue(i + S::kDepth);
+    }
+    if (i >= nfull) continue;  // wave-uniform: no tile of this wave at step i (barriers still counted)
+    const int tile = tb + KL * i + kl;
+    if (!interior(tile)) mask(tile, sa, xa);
+    uint32_t hw[8];
+    float lt;
+    if (i + 1 < nfull) {
+      read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xb);
+      // S^T of the next tile interleaved with this tile's probabilities
+      qk(xb, sb);
+      lt = probs(sa, hw);
+    } else {
+      lt = probs(sa, hw);
+    }
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kAcceptSum)) != 0) raise(sa, hw, lt);
+    lsum += lt;
+    pv(xa, hw);
+    xa = xb;
+    sa = sb;
+  }
+
+  // ---- merge the KL key lanes of each row tile in a fixed order
+  const float lrow = pair_sum(lsum);
+  if (hh == 0) {
+    sm_m[kl * kRows + r] = m_ref;
+    sm_l[kl * kRows + r] = lrow;
+  }
+  __syncthreads();  // also: every ring read is done, the ring area is free
+  float Mrow = sm_m[r];
+#pragma unroll
+  for (int k = 1; k < KL; ++k) Mrow = fmaxf(Mrow, sm_m[k * kRows + r]);
+  float Lrow = 0.f;
+#pragma unroll
+  for (int k = 0; k < KL; ++k) Lrow += sm_l[k * kRows + r] * __builtin_amdgcn_exp2f(sm_m[k * kRows + r] - Mrow);
+  const float asf = __builtin_amdgcn_exp2f(m_ref - Mrow);
+  // Output group gi = 4a + i holds dims 64a + 16i + 8hh + 0..7: elements 4i..4i+3 of d-tiles
+  // 2a and 2a + 1. Key lane kl owns groups kl*GPK .. +GPK-1 and receives them from the others.
+  constexpr int kGpk = 8 / KL;
+  float* xch = reinterpret_cast<float*>(body);  // [owner][rt][source][kGpk*8 floats][64 lanes]
+  auto xidx = [&](int owner, int src, int f) -> int { return (((owner * RT + rt) * KL + src) * (kGpk * 8) + f) * 64 + lane; };
+#pragma unroll
+  for (int gi = 0; gi < 8; ++gi) {
+    const int owner = gi / kGpk;
+    if (owner == kl) continue;
+    const int aa = gi >> 2, ii = gi & 3;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xch[xidx(owner, kl, (gi % kGpk) * 8 + bb * 4 + k)] = o[2 * aa + bb][4 * ii + k] * asf;
+  }
+  __syncthreads();
+  const bool direct = (nsplit == 1);
+  const float vsc = *a.v_scale;
+  const int64_t part = ((int64_t)b * a.num_kv_heads + g) * a.max_splits + s;
+  if (row_ok) {
+    const int i = r / G, hq = g * G + (r - i * G);
+    const float mul = Lrow > 0.f ? vsc / Lrow : 0.f;
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi) {
+      // compile-time group index (the accumulators are only indexed by constants)
+      if (gi / kGpk != kl) continue;
+      const int gl = gi % kGpk;
+      const int aa = gi >> 2, ii = gi & 3;
+      float o8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+#pragma unroll
+      for (int src = 0; src < KL; ++src) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float val = (src == kl) ? o[2 * aa + bb][4 * ii + k] * asf : xch[xidx(kl, src, gl * 8 + bb * 4 + k)];
+            o8[2 * k + bb] += val;
+          }
+      }
+      const int d0 = 64 * aa + 16 * ii + 8 * hh;
+      if (direct) {
+        float* op = a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + d0;
+        *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o8[0], o8[1], o8[2], o8[3]} * mul;
+        *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o8[4], o8[5], o8[6], o8[7]} * mul;
+      } else {
+        float* op = a.ws_o + (part * a.rows_pad + r) * kHeadDim + d0;
+        *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o8[0], o8[1], o8[2], o8[3]};
+        *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o8[4], o8[5], o8[6], o8[7]};
+      }
+    }
+    if (!direct && kl == 0 && hh == 0) {
+      a.ws_ml[part * 2 * a.rows_pad + r] = Mrow;
+      a.ws_ml[part * 2 * a.rows_pad + a.rows_pad + r] = Lrow;
+    }
+  }
+}
+
+}  // namespace
+
+template <int RT, int KL>
+static hipError_t launch_m32_t(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+  const int64_t grid = a.xcd_pairs ? (pairs + 7) / 8 * 8 * a.max_splits : pairs * a.max_splits;
+  hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true>), dim3((unsigned)grid), dim3(M32Shape<RT, KL, true>::kThreads),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_m32(const DecodeArgs& a, int rt, bool fp8, hipStream_t stream) {
+  if (!fp8) return hipErrorInvalidValue;
+  switch (rt) {
+    case 1: return launch_m32_t<1, 8>(a, stream);
+    case 2: return launch_m32_t<2, 4>(a, stream);
+    case 4: return launch_m32_t<4, 2>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fkv

@@ -31,10 +31,11 @@ def _check(lay, out, seqs=None, kv_heads=None, tol=parity.ATTN_TOL, label=""):
 
 
 def _layer(lay, **kw):
-    """Built PagedLayer, or None after checking that the layout rejects the row count
-    (layout 4 keeps two halves of the query rows, so it needs at least three row tiles)."""
+    """Built PagedLayer, or None after checking that the layout rejects the shape (layout 4
+    keeps two halves of the query rows, so it needs at least three row tiles; layout 5
+    reads FP8 caches only)."""
     nt = (lay.num_q_heads // lay.num_kv_heads * lay.q_len + 15) // 16
-    if kw.get("layout") == 4 and nt < 3:
+    if (kw.get("layout") == 4 and nt < 3) or (kw.get("layout") == 5 and lay.cache_dtype != "fp8_e4m3fn"):
         with pytest.raises(fkv.FkvError) as e:
             PagedLayer(lay, **kw)
         assert e.value.status == fkv.EUNSUPPORTED
@@ -54,7 +55,7 @@ def _workloads():
     yield "c4_draft_layer48", lambda: synth.c4_layer(48)
 
 
-@pytest.mark.parametrize("layout", [1, 2, 3, 4])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("name,make", list(_workloads()), ids=[n for n, _ in _workloads()])
 def test_workload_parity(name, make, layout):
     lay = make()
@@ -124,7 +125,7 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("layout", [1, 2, 3, 4])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("case", EDGE, ids=[f"L{c[0]}-M{c[1]}-w{c[2]}-{c[3]}x{c[4]}-p{c[5]}-{c[6][:4]}" for c in EDGE])
 def test_edge_cases(case, layout):
     seq_lens, M, wl, hq, hkv, bs, dt = case
@@ -138,7 +139,7 @@ def test_edge_cases(case, layout):
     _check(lay, out, label=f"{case} layout {layout}")
 
 
-@pytest.mark.parametrize("layout", [1, 3, 4])
+@pytest.mark.parametrize("layout", [1, 3, 4, 5])
 @pytest.mark.parametrize("split_tiles", [1, 2, 3, 8, 128])
 def test_split_granularity(split_tiles, layout):
     lay = synth.tiny_layer(77, [2000, 64, 900], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
