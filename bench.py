@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="layer copies to rotate over (0 = enough for 1 GiB)")
     p.add_argument("--split-tiles", type=int, default=0)
     p.add_argument("--layout", type=int, default=0, help="decode work-group layout (0 = automatic)")
+    p.add_argument("--row-groups", type=int, default=0, help="layout 5: row groups per split (0 = automatic)")
     p.add_argument("--cache-dtype", default="fp8_e4m3fn")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -63,13 +64,13 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
 
     lay = synth.make_layer(f"c3_m{args.q_len}_{context}_p{block_size}", 1003, 0, 72, 8, block_size, args.q_len, -1,
                            [context], cache_dtype=cache_dtype)
-    base = PagedLayer(lay, split_tiles=args.split_tiles, layout=args.layout).build()
+    base = PagedLayer(lay, split_tiles=args.split_tiles, layout=args.layout, row_groups=args.row_groups).build()
     kv_bytes, other = algorithmic_bytes(context, args.q_len, 72, 8, block_size, 1 if cache_dtype == "fp8_e4m3fn" else 2)
     pool_total = 2 * base.k_pool.numel()
     copies = args.copies or max(2, math.ceil((1 << 30) / kv_bytes))
     layers = [base]
     for _ in range(copies - 1):
-        c = PagedLayer(lay, poison=False, split_tiles=args.split_tiles, layout=args.layout)
+        c = PagedLayer(lay, poison=False, split_tiles=args.split_tiles, layout=args.layout, row_groups=args.row_groups)
         c.k_pool.copy_(base.k_pool)
         c.v_pool.copy_(base.v_pool)
         c.step_k, c.step_v, c.step_slots = base.step_k, base.step_v, base.step_slots
@@ -110,7 +111,7 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
     return dict(kv_bytes=kv_bytes, other_bytes=other, copies=copies, working_set=copies * kv_bytes,
                 wall_ms_per_step=wall * 1e3 / steps, step_ms=mean(step_ms), insert_ms=mean(ins_ms),
                 decode_ms=mean(dec_ms), decode_ms_median=med(dec_ms), plan_ws=base.workspace.numel(),
-                combine=cnt["decode_combine_launches"] > 0)
+                combine=cnt["decode_combine_launches"] > 0, fused=cnt["decode_combine_launches"] == 0)
 
 
 def cpu_baseline(seconds):
@@ -146,8 +147,8 @@ def cpu_baseline(seconds):
                       f"{el:.1f} s, {el / n * 1e3:.1f} ms/step"}
 
 
-# split kernel each decode layout launches (layout 0, the automatic choice, is the row-group kernel)
-DECODE_KERNELS = {0: "decode_rows_kernel", 1: "decode_split_dma_kernel", 2: "decode_split_kernel",
+# split kernel each decode layout launches (layout 0, the automatic choice, is the 32-row kernel for FP8)
+DECODE_KERNELS = {0: "decode_m32_kernel", 1: "decode_split_dma_kernel", 2: "decode_split_kernel",
                   3: "decode_rows_kernel", 4: "decode_wide_kernel", 5: "decode_m32_kernel"}
 
 
@@ -225,7 +226,8 @@ def main():
         "decode_kv_gbs": round(kv / (r["decode_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(src, cfg_name),
-                     "kernel": f"{DECODE_KERNELS[args.layout]} + decode_combine_kernel (one decode call)",
+                     "kernel": f"{DECODE_KERNELS[args.layout]}" + ("" if r["fused"] else " + decode_combine_kernel")
+                               + " (one decode call)",
                      "algorithmic_bytes": kv + r["other_bytes"]},
         "source_hash": src,
     }

@@ -96,14 +96,28 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   p->row_groups = 1;
   int64_t tps = d->split_tiles;
   if (sh.groups_per_cu == -2) {
-    // 32-row kernel: one work group per (sequence, KV head, split) holding every row; the
-    // splits fill the chip, each key lane takes whole tiles, a split at most 128 tiles
-    p->rows_pad = 32 * sh.r;
+    // 32-row kernel: the rows_pad = 32 * rt_total packed rows of a KV head are cut into RG
+    // row groups of separate work groups (on one XCD, sharing K/V tiles through its L2); the
+    // splits fill the chip, each key lane takes whole tiles, a split at most 128 tiles.
+    const int rt_total = sh.r;
+    p->rows_pad = 32 * rt_total;
+    if (d->row_groups != 0 && d->row_groups != 1 && d->row_groups != 2 && d->row_groups != 4) return FKV_EINVAL;
+    int rg = d->row_groups;
+    const int64_t bg = (int64_t)std::max(d->num_seqs, 1) * hkv;
+    if (rg == 0) {
+      // Automatic: two row groups whenever there are two row tiles. Each split partial costs
+      // 512 bytes per row written and read back, each K/V tile 8 KB per reading work group
+      // (the second reader hits the XCD's L2); measured on the 72/8-head layer at M = 12,
+      // two groups beat one and four at both 8k and 32k context.
+      rg = rt_total >= 2 ? 2 : 1;
+    }
+    if (rg > rt_total) return FKV_EUNSUPPORTED;
+    p->row_groups = rg;
+    const int kl = 8 / (rt_total / rg);
     if (tps == 0) {
-      const int64_t bg = (int64_t)std::max(d->num_seqs, 1) * hkv;
-      const int64_t splits = std::max<int64_t>(1, kNumCUs / bg);
+      const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * rg));
       tps = (tiles_max + splits - 1) / splits;
-      tps = (tps + sh.k - 1) / sh.k * sh.k;
+      tps = (tps + kl - 1) / kl * kl;
       tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
       tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
     }
@@ -141,6 +155,8 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   // Row-group kernel: with at least eight (sequence, KV head) pairs, each pair's work groups
   // go to one XCD (all eight XCDs stay busy); else each split's row groups share one.
   p->xcd_pairs = ((sh.groups_per_cu == 0 || sh.groups_per_cu == -2) && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
+  p->fused_combine = 0;
+  p->ws_ctl_bytes = 0;
   if (max_splits <= 1) {
     p->ws_o_bytes = p->ws_ml_bytes = p->ws_bytes = 0;
     return FKV_OK;
@@ -148,7 +164,16 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const uint64_t parts = (uint64_t)d->num_seqs * hkv * (uint64_t)max_splits;
   p->ws_o_bytes = round_up(parts * p->rows_pad * FKV_HEAD_DIM * sizeof(float), kAlign);
   p->ws_ml_bytes = round_up(parts * 2 * p->rows_pad * sizeof(float), kAlign);
-  p->ws_bytes = p->ws_o_bytes + p->ws_ml_bytes;
+  if (sh.groups_per_cu == -2) {
+    // 32-row kernel: when every work group of the grid fits on the chip at once (one per
+    // CU), the splits of a (sequence, KV head) are merged inside the kernel
+    const int64_t pairs = (int64_t)d->num_seqs * hkv;
+    const int64_t per_pair = max_splits * p->row_groups;
+    const int64_t grid = p->xcd_pairs ? (pairs + 7) / 8 * 8 * per_pair : pairs * per_pair;
+    p->fused_combine = grid <= kNumCUs ? 1 : 0;
+    p->ws_ctl_bytes = round_up((uint64_t)pairs * 256, kAlign);  // 256 bytes of counters per pair
+  }
+  p->ws_bytes = p->ws_o_bytes + p->ws_ml_bytes + p->ws_ctl_bytes;
   return FKV_OK;
 }
 
@@ -242,6 +267,9 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   a.out = static_cast<float*>(out);
   a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
+  a.ws_ctl = p.ws_ctl_bytes ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_o_bytes + p.ws_ml_bytes)
+                            : nullptr;
+  a.fused_combine = p.fused_combine;
   a.xcd_pairs = p.xcd_pairs;
   a.num_seqs = desc->num_seqs;
   a.num_q_heads = desc->num_q_heads;

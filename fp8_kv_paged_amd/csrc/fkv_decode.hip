@@ -941,14 +941,14 @@ hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool 
   if (shape.groups_per_cu == 0) {
     e = launch_rows(a, shape.ntw, fp8, stream);
   } else if (shape.groups_per_cu == -2) {
-    e = launch_m32(a, shape.r, fp8, stream);
+    e = launch_m32(a, shape.r / a.row_groups, fp8, stream);  // row tiles per work group
   } else if (shape.groups_per_cu < 0) {
     e = launch_wide(a, shape.ntw, fp8, stream);
   } else {
     e = fp8 ? dispatch_split<true>(a, shape, stream) : dispatch_split<false>(a, shape, stream);
   }
   if (e != hipSuccess) return e;
-  if (a.max_splits > 1) {
+  if (a.max_splits > 1 && !a.fused_combine) {
     e = shape.groups_per_cu == -1 ? launch_combine_lanes(a, fp8, stream) : launch_combine(a, fp8, stream);
     *launched_combine = true;
   }

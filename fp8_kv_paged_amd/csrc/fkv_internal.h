@@ -34,6 +34,8 @@ struct DecodePlan {
   int max_splits;      // grid x
   size_t ws_o_bytes;   // fp32 partial outputs
   size_t ws_ml_bytes;  // fp32 (m, l) per partial row
+  size_t ws_ctl_bytes; // uint32 control counters of the in-kernel split merge (4 per pair)
+  int fused_combine;   // layout 5 with the whole grid resident: splits merged inside the kernel
   int xcd_pairs;       // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   size_t ws_bytes;     // total, 256-byte aligned pieces
 };
@@ -49,10 +51,12 @@ struct DecodeArgs {
   float* out;
   float* ws_o;
   float* ws_ml;
+  uint32_t* ws_ctl;      // 4 counters per (sequence, KV head): started, finished, claimed, exited
   int32_t num_seqs, num_q_heads, num_kv_heads, group, q_len, block_size, max_blocks, num_blocks;
   int32_t window_left, tiles_per_split, max_splits, max_seq_len, rows_pad;
   int32_t row_groups;  // row-group kernel: groups of 16*ntw packed rows
   int32_t xcd_pairs;   // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
+  int32_t fused_combine;  // 32-row kernel: merge the splits inside the kernel (no combine launch)
   float softmax_scale;
 };
 
@@ -75,13 +79,13 @@ struct SplitShapeInfo {
 // rows cut into r tiles of 32 (1, 2 or 4) and the keys into k = 8 / r lanes
 // (groups_per_cu -2 marks it; ntw = r).
 inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
-  if (layout == 5) {
+  if (layout == 5 || (layout == 0 && fp8)) {  // layout 0 (automatic) is layout 5 for FP8 caches
     const int rows = 16 * nt;
     const int rt = rows <= 32 ? 1 : (rows <= 64 ? 2 : 4);
     return {rt, rt, 8 / rt, -2};
   }
   if (layout == 4 && nt >= 3) return {(nt + 1) / 2, 2, 2, -1};
-  if (layout == 3 || layout == 0) {  // layout 0 (automatic) is layout 3
+  if (layout == 3 || layout == 0) {  // layout 0 (automatic) is layout 3 for BF16 caches
     const int ntw = nt >= 2 ? 2 : 1;
     return {ntw, (nt + ntw - 1) / ntw, fp8 ? 8 : 4, 0};
   }

@@ -111,6 +111,85 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t
 // K row fed by A-operand row m of a 32-key tile: bits 2 and 3 of m swapped.
 __device__ __forceinline__ int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+// Split partials are written and read with the agent-coherence cache bit (sc1: written
+// through to, and read from, the memory side), so the work groups that merge them need no
+// L2 write-back or invalidate; counters alone order the accesses.
+constexpr int kCoherent = 16;  // cache-policy bits of the buffer intrinsics: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+constexpr int kSpinLimit = 1 << 15;  // polls (each with a short sleep) before a waiting group gives up
+constexpr int kCtlStride = 64;       // uint32 per pair: its four counters alone in a 256-byte block
+
+// Merges the split partials of output quads [q0, q0 + count) of one (sequence, KV head)
+// (quad q = packed row q / 32, dims 4(q % 32) .. +3): out = v_scale * sum_s w_s O_s / sum_s
+// w_s l_s with w_s = 2^(m_s - max_s m_s), sums in split order. The rows' (m, l) pairs are
+// read once into LDS and their weights computed once per (row, split); each thread then
+// requests its quad of every split at once.
+template <int kThreads>
+__device__ __forceinline__ void merge_slice(const DecodeArgs& a, int b, int g, int nsplit, int q0, int count, float vsc,
+                                            float* wsm) {
+  const int G = a.group, M = a.q_len, GM = G * M;
+  const int r0 = q0 >> 5, r1 = min((q0 + count - 1) >> 5, GM - 1);
+  const int nr = r1 - r0 + 1;
+  const int64_t base = ((int64_t)b * a.num_kv_heads + g) * a.max_splits;
+  const uint32_t o_bytes = (uint32_t)((int64_t)nsplit * a.rows_pad * kHeadDim * 4);
+  const uint32_t ml_bytes = (uint32_t)((int64_t)nsplit * 2 * a.rows_pad * 4);
+  const __amdgpu_buffer_rsrc_t orsrc = coherent_rsrc(a.ws_o + base * a.rows_pad * kHeadDim, o_bytes);
+  const __amdgpu_buffer_rsrc_t mlrsrc = coherent_rsrc(a.ws_ml + base * 2 * a.rows_pad, ml_bytes);
+  float* wm = wsm;                 // [nr][nsplit]: m, then the weight
+  float* wl = wsm + nr * nsplit;   // [nr][nsplit]: l
+  float* mul = wl + nr * nsplit;   // [nr]: v_scale / sum_s w_s l_s
+  for (int idx = threadIdx.x; idx < nr * nsplit; idx += kThreads) {
+    const int rr = idx / nsplit, sj = idx % nsplit;
+    const int off = (sj * 2 * a.rows_pad + r0 + rr) * 4;
+    wm[idx] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mlrsrc, off, 0, kCoherent));
+    wl[idx] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mlrsrc, off + a.rows_pad * 4, 0, kCoherent));
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nr) {
+    float* m = wm + threadIdx.x * nsplit;
+    const float* l = wl + threadIdx.x * nsplit;
+    float mx = -INFINITY;
+    for (int sj = 0; sj < nsplit; ++sj) mx = fmaxf(mx, m[sj]);
+    float lsum = 0.f;
+    for (int sj = 0; sj < nsplit; ++sj) {
+      const float wgt = __builtin_amdgcn_exp2f(m[sj] - mx);
+      m[sj] = wgt;
+      lsum += wgt * l[sj];
+    }
+    mul[threadIdx.x] = lsum > 0.f ? vsc / lsum : 0.f;
+  }
+  __syncthreads();
+  constexpr int kChunk = 32;
+  for (int t = (int)threadIdx.x; t < count; t += kThreads) {
+    const int q = q0 + t, r = q >> 5, d4 = q & 31;
+    if (r >= GM) continue;
+    const float* wr = wm + (r - r0) * nsplit;
+    const int o_off = (r * kHeadDim + 4 * d4) * 4, o_stride = a.rows_pad * kHeadDim * 4;
+    f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += kChunk) {
+      f32x4_t os[kChunk];
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const int sj = min(s0 + j, nsplit - 1);  // clamped: in-range loads, unused past the end
+        os[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(orsrc, o_off + sj * o_stride, 0, kCoherent));
+      }
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j)
+        if (s0 + j < nsplit) acc += os[j] * wr[s0 + j];
+    }
+    const int i = r / G, hq = g * G + (r - i * G);
+    *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) =
+        acc * mul[r - r0];
+  }
+  __syncthreads();  // the LDS weights are free again
+}
+
+}  // namespace
+
+namespace {
 
 template <int RT, int KL, bool kFp8>
 __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_m32_kernel(DecodeArgs a) {
@@ -127,15 +206,19 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 
   // ---- (sequence, KV head, split); with >= 8 pairs every split of a pair on one XCD
   const int x = blockIdx.x;
-  int bg, s;
+  const int RG = a.row_groups;   // work groups per (sequence, KV head, split), kRows rows each
+  const int per_pair = a.max_splits * RG;
+  int bg, rem;
   if (a.xcd_pairs) {
     const int slot = x >> 3;
-    bg = (slot / a.max_splits) * 8 + (x & 7);
-    s = slot % a.max_splits;
+    bg = (slot / per_pair) * 8 + (x & 7);
+    rem = slot % per_pair;
   } else {
-    bg = x / a.max_splits;
-    s = x % a.max_splits;
+    bg = x / per_pair;
+    rem = x % per_pair;
   }
+  const int s = rem / RG, rg = rem % RG;
+  const int row0 = rg * kRows;   // first packed row of this work group
   if (bg >= a.num_seqs * a.num_kv_heads) return;
   const int g = bg % a.num_kv_heads, b = bg / a.num_kv_heads;
 
@@ -165,8 +248,8 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   const int ntiles = max(0, t_end - t_first);
   const int nsplit = (ntiles + tps - 1) / tps;
   if (ntiles == 0) {
-    // no visible key for any row: split 0 writes the rows as zeros
-    if (s == 0) {
+    // no visible key for any row: split 0, row group 0 writes the rows as zeros
+    if (s == 0 && rg == 0) {
       for (int idx = threadIdx.x; idx < GM * (kHeadDim / 4); idx += S::kThreads) {
         const int r = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
         const int i = r / G, hq = g * G + (r - i * G);
@@ -177,6 +260,11 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
     return;
   }
   if (s >= nsplit) return;
+  // in-kernel split merge: count the resident work groups of the pair
+  uint32_t* const ctl = a.ws_ctl + kCtlStride * (int64_t)bg;  // started, finished, claimed, exited
+  const bool fused = a.fused_combine && nsplit > 1;
+  const int group_wgs = nsplit * RG;  // work groups that write partials of this pair
+  if (fused && threadIdx.x == 0) __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int tb = t_first + s * tps;
   const int te = min(tb + tps, t_end);
   if (wl >= 0) {
@@ -189,10 +277,11 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   float ks = *a.k_scale;
 
   // ---- this wave's query rows and Q operand: lane (n, hh) holds dims 32j + 16hh .. +15
-  const int r = 32 * rt + n;
+  const int rl = 32 * rt + n;  // row within the work group (LDS index)
+  const int r = row0 + rl;      // packed row of the KV head
   const bool row_ok = r < GM;
   const int rpos = row_ok ? L - M + r / G : -1;
-  const bool wave_rows = 32 * rt < GM;  // wave-uniform: the row tile holds a real row
+  const bool wave_rows = row0 + 32 * rt < GM;  // wave-uniform: the row tile holds a real row
   u32x4_t qraw[8];
   if (row_ok) {
     const int i = r / G, hq = g * G + (r - i * G);
@@ -405,16 +494,16 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   // ---- merge the KL key lanes of each row tile in a fixed order
   const float lrow = pair_sum(lsum);
   if (hh == 0) {
-    sm_m[kl * kRows + r] = m_ref;
-    sm_l[kl * kRows + r] = lrow;
+    sm_m[kl * kRows + rl] = m_ref;
+    sm_l[kl * kRows + rl] = lrow;
   }
   __syncthreads();  // also: every ring read is done, the ring area is free
-  float Mrow = sm_m[r];
+  float Mrow = sm_m[rl];
 #pragma unroll
-  for (int k = 1; k < KL; ++k) Mrow = fmaxf(Mrow, sm_m[k * kRows + r]);
+  for (int k = 1; k < KL; ++k) Mrow = fmaxf(Mrow, sm_m[k * kRows + rl]);
   float Lrow = 0.f;
 #pragma unroll
-  for (int k = 0; k < KL; ++k) Lrow += sm_l[k * kRows + r] * __builtin_amdgcn_exp2f(sm_m[k * kRows + r] - Mrow);
+  for (int k = 0; k < KL; ++k) Lrow += sm_l[k * kRows + rl] * __builtin_amdgcn_exp2f(sm_m[k * kRows + rl] - Mrow);
   const float asf = __builtin_amdgcn_exp2f(m_ref - Mrow);
   // Output group gi = 4a + i holds dims 64a + 16i + 8hh + 0..7: elements 4i..4i+3 of d-tiles
   // 2a and 2a + 1. Key lane kl owns groups kl*GPK .. +GPK-1 and receives them from the others.
@@ -435,42 +524,121 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   const bool direct = (nsplit == 1);
   const float vsc = *a.v_scale;
   const int64_t part = ((int64_t)b * a.num_kv_heads + g) * a.max_splits + s;
-  if (row_ok) {
-    const int i = r / G, hq = g * G + (r - i * G);
-    const float mul = Lrow > 0.f ? vsc / Lrow : 0.f;
+  // The owners sum their groups over the key lanes in lane order, then the merged rows are
+  // staged row-major in LDS (rows padded to kStageStride floats: conflict-free) so that the
+  // group's stores write whole contiguous rows.
+  constexpr int kStageStride = kHeadDim + 4;
+  float o8s[kGpk][8];
 #pragma unroll
-    for (int gi = 0; gi < 8; ++gi) {
-      // compile-time group index (the accumulators are only indexed by constants)
-      if (gi / kGpk != kl) continue;
-      const int gl = gi % kGpk;
-      const int aa = gi >> 2, ii = gi & 3;
-      float o8[8];
+  for (int gi = 0; gi < 8; ++gi) {
+    // compile-time group index (the accumulators are only indexed by constants)
+    if (gi / kGpk != kl) continue;
+    const int gl = gi % kGpk;
+    const int aa = gi >> 2, ii = gi & 3;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+    for (int e = 0; e < 8; ++e) o8s[gl][e] = 0.f;
 #pragma unroll
-      for (int src = 0; src < KL; ++src) {
+    for (int src = 0; src < KL; ++src) {
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float val = (src == kl) ? o[2 * aa + bb][4 * ii + k] * asf : xch[xidx(kl, src, gl * 8 + bb * 4 + k)];
-            o8[2 * k + bb] += val;
+        for (int k = 0; k < 4; ++k) {
+          const float val = (src == kl) ? o[2 * aa + bb][4 * ii + k] * asf : xch[xidx(kl, src, gl * 8 + bb * 4 + k)];
+          o8s[gl][2 * k + bb] += val;
+        }
+    }
+  }
+  float* stage = reinterpret_cast<float*>(body);  // [kRows][kStageStride], over the exchange area
+  float* sm_row = sm_ml;                          // merged (M, L) per row, over the per-lane (m, l)
+  __syncthreads();  // every exchange and (m, l) read is done
+#pragma unroll
+  for (int gl = 0; gl < kGpk; ++gl) {
+    const int gi = kl * kGpk + gl;
+    const int d0 = 64 * (gi >> 2) + 16 * (gi & 3) + 8 * hh;
+    float* st = stage + rl * kStageStride + d0;
+    *reinterpret_cast<f32x4_t*>(st) = f32x4_t{o8s[gl][0], o8s[gl][1], o8s[gl][2], o8s[gl][3]};
+    *reinterpret_cast<f32x4_t*>(st + 4) = f32x4_t{o8s[gl][4], o8s[gl][5], o8s[gl][6], o8s[gl][7]};
+  }
+  if (kl == 0 && hh == 0) {
+    sm_row[rl] = Mrow;
+    sm_row[kRows + rl] = Lrow;
+  }
+  __syncthreads();
+  const int nrows = max(0, min(kRows, GM - row0));  // real rows of this work group
+  if (direct) {
+    for (int idx = threadIdx.x; idx < nrows * (kHeadDim / 4); idx += S::kThreads) {
+      const int rr = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      const int i = (row0 + rr) / G, hq = g * G + (row0 + rr - i * G);
+      const float lw = sm_row[kRows + rr];
+      const float mul = lw > 0.f ? vsc / lw : 0.f;
+      *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) =
+          *reinterpret_cast<const f32x4_t*>(stage + rr * kStageStride + 4 * d4) * mul;
+    }
+  } else {
+    // the partial: rows_pad x 128 fp32 (only the GM real rows written), then (M, L) per row
+    const __amdgpu_buffer_rsrc_t prsrc =
+        coherent_rsrc(a.ws_o + part * a.rows_pad * kHeadDim, (uint32_t)(a.rows_pad * kHeadDim * 4));
+    for (int idx = threadIdx.x; idx < nrows * (kHeadDim / 4); idx += S::kThreads) {
+      const int rr = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + rr * kStageStride + 4 * d4);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prsrc, (row0 * (kHeadDim / 4) + idx) * 16, 0,
+                                             kCoherent);
+    }
+    const __amdgpu_buffer_rsrc_t mlrsrc = coherent_rsrc(a.ws_ml + part * 2 * a.rows_pad, 2 * a.rows_pad * 4);
+    for (int idx = threadIdx.x; idx < 2 * nrows; idx += S::kThreads) {
+      const int which = idx / nrows, rr = idx % nrows;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sm_row[which * kRows + rr]), mlrsrc,
+                                            (which * a.rows_pad + row0 + rr) * 4, 0, kCoherent);
+    }
+  }
+
+  // ---- in-kernel merge of the pair's splits (grids that fit on the chip at once). A work
+  // group waits for the other splits only when all of them have started, i.e. are resident
+  // and will finish without needing this CU; the last split to finish always takes every
+  // output slice nobody has claimed, so waiting is never needed for completion. The last
+  // work group to leave returns the counters to zero for the next call.
+  if (fused) {
+    __shared__ int sh_role, sh_slice;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's coherent partial stores are done
+    __syncthreads();                                   // ... and every other thread's
+    if (threadIdx.x == 0) {
+      const uint32_t ns = (uint32_t)group_wgs;
+      const uint32_t f = __hip_atomic_fetch_add(&ctl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int role = (f == ns - 1) ? 1 : 0;
+      if (!role && __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
+        for (int it = 0; it < kSpinLimit; ++it) {
+          if (__hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
+            role = 1;
+            break;
           }
+          __builtin_amdgcn_s_sleep(4);
+        }
       }
-      const int d0 = 64 * aa + 16 * ii + 8 * hh;
-      if (direct) {
-        float* op = a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + d0;
-        *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o8[0], o8[1], o8[2], o8[3]} * mul;
-        *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o8[4], o8[5], o8[6], o8[7]} * mul;
-      } else {
-        float* op = a.ws_o + (part * a.rows_pad + r) * kHeadDim + d0;
-        *reinterpret_cast<f32x4_t*>(op) = f32x4_t{o8[0], o8[1], o8[2], o8[3]};
-        *reinterpret_cast<f32x4_t*>(op + 4) = f32x4_t{o8[4], o8[5], o8[6], o8[7]};
+      sh_role = role;  // the merge reads the partials with coherent loads issued after this point
+    }
+    __syncthreads();
+    if (sh_role) {
+      // one slice of consecutive output quads per split (at most kThreads quads each)
+      const int quads = GM * 32;
+      const int per = max((quads + group_wgs - 1) / group_wgs, (quads + 255) / 256);
+      const int nslices = (quads + per - 1) / per;
+      for (;;) {
+        if (threadIdx.x == 0)
+          sh_slice = (int)__hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int slice = sh_slice;
+        __syncthreads();
+        if (slice >= nslices) break;
+        merge_slice<S::kThreads>(a, b, g, nsplit, slice * per, min(per, quads - slice * per), vsc,
+                                 reinterpret_cast<float*>(body));
       }
     }
-    if (!direct && kl == 0 && hh == 0) {
-      a.ws_ml[part * 2 * a.rows_pad + r] = Mrow;
-      a.ws_ml[part * 2 * a.rows_pad + a.rows_pad + r] = Lrow;
+    if (threadIdx.x == 0) {
+      const uint32_t e = __hip_atomic_fetch_add(&ctl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (e == (uint32_t)group_wgs - 1) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) __hip_atomic_store(&ctl[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 }
@@ -480,7 +648,8 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 template <int RT, int KL>
 static hipError_t launch_m32_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
-  const int64_t grid = a.xcd_pairs ? (pairs + 7) / 8 * 8 * a.max_splits : pairs * a.max_splits;
+  const int64_t per_pair = (int64_t)a.max_splits * a.row_groups;
+  const int64_t grid = a.xcd_pairs ? (pairs + 7) / 8 * 8 * per_pair : pairs * per_pair;
   hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true>), dim3((unsigned)grid), dim3(M32Shape<RT, KL, true>::kThreads),
                      0, stream, a);
   return hipGetLastError();

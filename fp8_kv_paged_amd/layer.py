@@ -22,7 +22,7 @@ def to_dev_bits(bits, device):
 
 
 class PagedLayer:
-    def __init__(self, lay, device="cuda", poison=True, split_tiles=0, layout=0):
+    def __init__(self, lay, device="cuda", poison=True, split_tiles=0, layout=0, row_groups=0):
         self.lay = lay
         self.device = device
         self.desc = fkv.make_cache_desc(lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.cache_dtype)
@@ -37,19 +37,20 @@ class PagedLayer:
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(lay.seq_lens)).to(device)
         self.max_seq_len = int(max(1, lay.seq_lens.max())) if lay.num_seqs else 1
         self.ddesc = fkv.make_decode_desc(lay.num_seqs, lay.q_len, lay.num_q_heads, lay.max_blocks, self.max_seq_len,
-                                          lay.window_left, lay.softmax_scale, split_tiles, layout)
+                                          lay.window_left, lay.softmax_scale, split_tiles, layout, row_groups)
         self.q = to_dev_bits(lay.q_bits(), device)
         self.out = torch.empty((lay.num_seqs, lay.q_len, lay.num_q_heads, HEAD_DIM), dtype=torch.float32,
                                device=device)
         nws = fkv.decode_workspace_bytes(self.cache, self.ddesc)
-        self.workspace = torch.empty((max(nws, 16),), dtype=torch.uint8, device=device)
+        # zero once: the split-merge counters at its end must start at zero (calls leave them so)
+        self.workspace = torch.zeros((max(nws, 16),), dtype=torch.uint8, device=device)
         self.step_k = self.step_v = self.step_slots = None
 
     def set_split_tiles(self, split_tiles):
         self.ddesc.split_tiles = int(split_tiles)
         nws = fkv.decode_workspace_bytes(self.cache, self.ddesc)
         if nws > self.workspace.numel():
-            self.workspace = torch.empty((nws,), dtype=torch.uint8, device=self.device)
+            self.workspace = torch.zeros((nws,), dtype=torch.uint8, device=self.device)
 
     def insert_tokens(self, b, t0, t1, chunk=32768):
         """Insert tokens [t0, t1) of sequence b (host-generated BF16) through the slot mapping."""

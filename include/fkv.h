@@ -148,6 +148,8 @@ typedef struct fkv_decode_desc {
                                   the query rows x two key lanes, one wave per SIMD, the
                                   output accumulators in AGPRs (3 to 7 row tiles, else
                                   FKV_EUNSUPPORTED)                                        */
+  int32_t row_groups;          /* layout 5: work groups sharing one split's query rows (1, 2
+                                  or 4; 0 = automatic); ignored by the other layouts       */
 } fkv_decode_desc;
 
 /*

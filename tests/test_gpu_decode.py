@@ -92,7 +92,7 @@ def test_c5_batched_parity_fp8(c5_fp8, q_len):
     ddesc = fkv.make_decode_desc(lay.num_seqs, q_len, 72, lay.max_blocks, int(lay.seq_lens.max()))
     q = to_dev_bits(lay.q_bits(), "cuda")
     out = torch.empty((lay.num_seqs, q_len, 72, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty((max(16, fkv.decode_workspace_bytes(gl.cache, ddesc)),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((max(16, fkv.decode_workspace_bytes(gl.cache, ddesc)),), dtype=torch.uint8, device="cuda")
     fkv.decode_attn(gl.cache, ddesc, q, gl.block_table, gl.seq_lens, gl.k_scale, gl.v_scale, out, ws)
     torch.cuda.synchronize()
     _check(lay, out, seqs=_c5_samples(lay), kv_heads=[0, 5], label=f"c5 fp8 M={q_len}")
@@ -176,7 +176,7 @@ def test_verify_rows_match_single_query_calls():
         q1 = to_dev_bits(lay.q_bits()[:, i:i + 1], "cuda")
         o1 = torch.empty((1, 1, 18, 128), dtype=torch.float32, device="cuda")
         sl = torch.tensor([L - M + i + 1], dtype=torch.int32, device="cuda")
-        ws = torch.empty((max(16, fkv.decode_workspace_bytes(gl.cache, d1)),), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros((max(16, fkv.decode_workspace_bytes(gl.cache, d1)),), dtype=torch.uint8, device="cuda")
         fkv.decode_attn(gl.cache, d1, q1, gl.block_table, sl, gl.k_scale, gl.v_scale, o1, ws)
         worst = max(worst, float(np.abs(o1.cpu().numpy()[0, 0] - out[0, i]).max()))
     print(f"[decode] M12 row vs q1 call max abs difference {worst:.3e}", flush=True)
@@ -198,3 +198,30 @@ def test_unsupported_packing_fails_closed():
     with pytest.raises(fkv.FkvError) as e:
         PagedLayer(lay)
     assert e.value.status == fkv.EUNSUPPORTED
+
+
+def test_fused_split_merge_is_deterministic_and_leaves_counters_zero():
+    """Layout 5 merges the splits inside the kernel when the grid fits on the chip: repeated
+    calls give bitwise-identical outputs and return the workspace's counters to zero."""
+    lay = synth.tiny_layer(99, [3000] * 8, num_q_heads=72, num_kv_heads=8, block_size=64, q_len=12)
+    gl = PagedLayer(lay, layout=5).build()
+    outs = [gl.decode().clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    pairs = lay.num_seqs * lay.num_kv_heads
+    nws = fkv.decode_workspace_bytes(gl.cache, gl.ddesc)
+    ctl_bytes = pairs * 256
+    assert torch.count_nonzero(gl.workspace[nws - ctl_bytes:nws]).item() == 0
+    _check(lay, outs[0], label="fused split merge")
+
+
+@pytest.mark.parametrize("row_groups", [1, 2, 4])
+@pytest.mark.parametrize("name,make", [("c2", synth.c2_layer), ("c3_8k_p64", lambda: synth.c3_layer(8192, 64)),
+                                       ("c4_sw_layer0", lambda: synth.c4_layer(0))], ids=["c2", "c3_8k_p64", "c4_sw"])
+def test_row_groups_parity(name, make, row_groups):
+    """Layout 5 with the query rows of a split cut over 1, 2 or 4 work groups."""
+    lay = make()
+    gl = PagedLayer(lay, layout=5, row_groups=row_groups).build()
+    out = gl.decode()
+    torch.cuda.synchronize()
+    _check(lay, out, label=f"{name} layout 5 row groups {row_groups}")
