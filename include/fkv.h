@@ -138,8 +138,9 @@ typedef struct fkv_decode_desc {
   float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
   int32_t out_dtype;           /* FKV_OUT_F32                                               */
   int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
-                                  (at most 128 with layouts 0, 1, 3 and 4)                  */
-  int32_t layout;              /* work-group layout: 0 = automatic (layout 3); 1 = query rows spread over
+                                  (at most 128 with layouts 0, 1, 3, 4 and 5)               */
+  int32_t layout;              /* work-group layout: 0 = automatic (layout 5 for an FP8 cache,
+                                  layout 3 for a BF16 cache); 1 = query rows spread over
                                   row groups of at most 32 rows per wave (two waves per SIMD);
                                   2 = all query rows of a KV head in every wave (one per SIMD);
                                   3 = row groups of at most 32 rows in separate work groups
@@ -147,15 +148,23 @@ typedef struct fkv_decode_desc {
                                   4 = one work group of four waves per split: two halves of
                                   the query rows x two key lanes, one wave per SIMD, the
                                   output accumulators in AGPRs (3 to 7 row tiles, else
-                                  FKV_EUNSUPPORTED)                                        */
+                                  FKV_EUNSUPPORTED);
+                                  5 = 32-row tiles (MFMA 32x32x16), eight waves per work
+                                  group, the split's rows in row_groups work groups on one
+                                  XCD; splits merged inside the kernel when the grid fits on
+                                  the chip (FP8 cache only, else FKV_EUNSUPPORTED)          */
   int32_t row_groups;          /* layout 5: work groups sharing one split's query rows (1, 2
-                                  or 4; 0 = automatic); ignored by the other layouts       */
+                                  or 4, at most the number of 32-row tiles; 0 = automatic);
+                                  ignored by the other layouts                              */
 } fkv_decode_desc;
 
 /*
  * Bytes of device workspace fkv_decode_attn needs for (cache, desc): split-KV
- * partial results. Pure host arithmetic; may be 0. Errors as fkv_decode_attn's
- * validation.
+ * partial results and, for layout 5, 256 bytes of merge counters per (sequence,
+ * KV head) at its end. Pure host arithmetic; may be 0. The workspace must be
+ * zero-filled once before its first use (the counters must start at zero); every
+ * call returns the counters to zero, so it can then be reused without clearing.
+ * One call at a time may use a workspace. Errors as fkv_decode_attn's validation.
  */
 int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* desc, size_t* bytes);
 
@@ -182,9 +191,13 @@ int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* de
  * seq_lens above the documented bound are clamped to it; block ids outside
  * [0, num_blocks) make their 32-key tile invisible (no out-of-pool read).
  * Reads only the cache, q, the metadata and the scales; writes only out and
- * the workspace. The result is bitwise reproducible for a given input and
- * split_tiles. Errors: FKV_EINVAL, FKV_EUNSUPPORTED (shape not compiled),
- * FKV_EWORKSPACE, FKV_EHIP.
+ * the workspace. The result is bitwise reproducible for a given input, layout,
+ * row_groups and split_tiles. Layout 5 merges the split partials inside its own
+ * kernel when every work group of the grid fits on the chip at once (one per CU):
+ * a work group waits for the other splits of its (sequence, KV head) only when all
+ * of them have started, and the last one to finish completes the merge, so no call
+ * depends on co-residency. Errors: FKV_EINVAL (also: row_groups not in {0, 1, 2,
+ * 4}), FKV_EUNSUPPORTED (shape not compiled), FKV_EWORKSPACE, FKV_EHIP.
  */
 int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
                     const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
