@@ -598,13 +598,21 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   // output slice nobody has claimed, so waiting is never needed for completion. The last
   // work group to leave returns the counters to zero for the next call.
   if (fused) {
+    // Roles: the last work group to finish (finish ticket ns - 1) claims slices until none is
+    // left; a work group that saw every split started waits (bounded) for the others and then
+    // merges the one slice it claims; any other leaves at once. Every slice index is claimed
+    // exactly once, and the last one takes whatever nobody else claimed, so every output quad
+    // is written once and no wait is needed for completion.
     __shared__ int sh_role, sh_slice;
+    const int quads = GM * 32;
+    const int per = max((quads + group_wgs - 1) / group_wgs, (quads + 255) / 256);
+    const int nslices = (quads + per - 1) / per;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's coherent partial stores are done
     __syncthreads();                                   // ... and every other thread's
     if (threadIdx.x == 0) {
       const uint32_t ns = (uint32_t)group_wgs;
       const uint32_t f = __hip_atomic_fetch_add(&ctl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int role = (f == ns - 1) ? 1 : 0;
+      int role = (f == ns - 1) ? 2 : 0;  // 0: leave, 1: merge one slice, 2: merge until none is left
       if (!role && __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
         for (int it = 0; it < kSpinLimit; ++it) {
           if (__hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
@@ -614,24 +622,23 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
           __builtin_amdgcn_s_sleep(4);
         }
       }
-      sh_role = role;  // the merge reads the partials with coherent loads issued after this point
+      // the merge reads the partials with coherent loads issued after this point
+      sh_slice = role ? (int)__hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : nslices;
+      sh_role = role;
     }
     __syncthreads();
-    if (sh_role) {
-      // one slice of consecutive output quads per split (at most kThreads quads each)
-      const int quads = GM * 32;
-      const int per = max((quads + group_wgs - 1) / group_wgs, (quads + 255) / 256);
-      const int nslices = (quads + per - 1) / per;
-      for (;;) {
-        if (threadIdx.x == 0)
-          sh_slice = (int)__hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const int slice = sh_slice;
-        __syncthreads();
-        if (slice >= nslices) break;
-        merge_slice<S::kThreads>(a, b, g, nsplit, slice * per, min(per, quads - slice * per), vsc,
-                                 reinterpret_cast<float*>(body));
-      }
+    const int role = sh_role;
+    int slice = sh_slice;
+    __syncthreads();
+    while (role != 0 && slice < nslices) {
+      merge_slice<S::kThreads>(a, b, g, nsplit, slice * per, min(per, quads - slice * per), vsc,
+                               reinterpret_cast<float*>(body));
+      if (role == 1) break;
+      if (threadIdx.x == 0)
+        sh_slice = (int)__hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      slice = sh_slice;
+      __syncthreads();
     }
     if (threadIdx.x == 0) {
       const uint32_t e = __hip_atomic_fetch_add(&ctl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
