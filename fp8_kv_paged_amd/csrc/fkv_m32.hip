@@ -120,7 +120,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, u
 }
 
 constexpr int kSpinLimit = 1 << 15;  // polls (each with a short sleep) before a waiting group gives up
-constexpr int kCtlStride = 64;       // uint32 per pair: its four counters alone in a 256-byte block
+// Per pair, alone in a 256-byte block: counters of started, finished and exited work groups,
+// then one claim bit per output slice (at most 256 slices).
+constexpr int kCtlStride = 64;
+constexpr int kCtlStarted = 0, kCtlFinished = 1, kCtlExited = 2, kCtlClaim = 8;
+constexpr int kFastSplits = 16;  // split counts whose partials one thread requests at once
 
 // Merges the split partials of output quads [q0, q0 + count) of one (sequence, KV head)
 // (quad q = packed row q / 32, dims 4(q % 32) .. +3): out = v_scale * sum_s w_s O_s / sum_s
@@ -185,6 +189,54 @@ __device__ __forceinline__ void merge_slice(const DecodeArgs& a, int b, int g, i
         acc * mul[r - r0];
   }
   __syncthreads();  // the LDS weights are free again
+}
+
+// One output quad merged from at most kFastSplits partials by one thread: every load is
+// requested at once (quad_issue) and combined later (quad_finish), with the same sums in
+// the same order as merge_slice.
+struct QuadLoads {
+  f32x4_t o[kFastSplits];
+  float m[kFastSplits], l[kFastSplits];
+};
+__device__ __forceinline__ void quad_issue(const DecodeArgs& a, int b, int g, int nsplit, int q, QuadLoads& x) {
+  const int r = q >> 5, d4 = q & 31;
+  const int64_t base = ((int64_t)b * a.num_kv_heads + g) * a.max_splits;
+  const __amdgpu_buffer_rsrc_t orsrc = coherent_rsrc(a.ws_o + base * a.rows_pad * kHeadDim,
+                                                     (uint32_t)((int64_t)nsplit * a.rows_pad * kHeadDim * 4));
+  const __amdgpu_buffer_rsrc_t mlrsrc =
+      coherent_rsrc(a.ws_ml + base * 2 * a.rows_pad, (uint32_t)((int64_t)nsplit * 2 * a.rows_pad * 4));
+  const int o_off = (r * kHeadDim + 4 * d4) * 4, o_stride = a.rows_pad * kHeadDim * 4;
+#pragma unroll
+  for (int j = 0; j < kFastSplits; ++j) {
+    const int sj = min(j, nsplit - 1);  // clamped: in-range loads, unused past the end
+    x.o[j] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(orsrc, o_off + sj * o_stride, 0, kCoherent));
+    x.m[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(mlrsrc, (sj * 2 * a.rows_pad + r) * 4, 0, kCoherent));
+    x.l[j] = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(mlrsrc, (sj * 2 * a.rows_pad + a.rows_pad + r) * 4, 0, kCoherent));
+  }
+}
+__device__ __forceinline__ void quad_finish(const DecodeArgs& a, int b, int g, int nsplit, int q, const QuadLoads& x,
+                                            float vsc) {
+  const int r = q >> 5, d4 = q & 31;
+  if (r >= a.group * a.q_len) return;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kFastSplits; ++j)
+    if (j < nsplit) mx = fmaxf(mx, x.m[j]);
+  float w[kFastSplits];
+  float lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kFastSplits; ++j) {
+    w[j] = __builtin_amdgcn_exp2f(x.m[j] - mx);
+    if (j < nsplit) lsum += w[j] * x.l[j];
+  }
+  const float mul = lsum > 0.f ? vsc / lsum : 0.f;
+  f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kFastSplits; ++j)
+    if (j < nsplit) acc += x.o[j] * w[j];
+  const int G = a.group, i = r / G, hq = g * G + (r - i * G);
+  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * a.q_len + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) = acc * mul;
 }
 
 }  // namespace
@@ -264,7 +316,8 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   uint32_t* const ctl = a.ws_ctl + kCtlStride * (int64_t)bg;  // started, finished, claimed, exited
   const bool fused = a.fused_combine && nsplit > 1;
   const int group_wgs = nsplit * RG;  // work groups that write partials of this pair
-  if (fused && threadIdx.x == 0) __hip_atomic_fetch_add(&ctl[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (fused && threadIdx.x == 0)
+    __hip_atomic_fetch_add(&ctl[kCtlStarted], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int tb = t_first + s * tps;
   const int te = min(tb + tps, t_end);
   if (wl >= 0) {
@@ -508,17 +561,22 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   // Output group gi = 4a + i holds dims 64a + 16i + 8hh + 0..7: elements 4i..4i+3 of d-tiles
   // 2a and 2a + 1. Key lane kl owns groups kl*GPK .. +GPK-1 and receives them from the others.
   constexpr int kGpk = 8 / KL;
-  float* xch = reinterpret_cast<float*>(body);  // [owner][rt][source][kGpk*8 floats][64 lanes]
-  auto xidx = [&](int owner, int src, int f) -> int { return (((owner * RT + rt) * KL + src) * (kGpk * 8) + f) * 64 + lane; };
+  // [owner][rt][source][kGpk*2 quads][64 lanes][4 floats]: 16-byte, lane-contiguous accesses
+  f32x4_t* xch = reinterpret_cast<f32x4_t*>(body);
+  auto xidx = [&](int owner, int src, int f4) -> int {
+    return (((owner * RT + rt) * KL + src) * (kGpk * 2) + f4) * 64 + lane;
+  };
 #pragma unroll
   for (int gi = 0; gi < 8; ++gi) {
     const int owner = gi / kGpk;
     if (owner == kl) continue;
     const int aa = gi >> 2, ii = gi & 3;
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) xch[xidx(owner, kl, (gi % kGpk) * 8 + bb * 4 + k)] = o[2 * aa + bb][4 * ii + k] * asf;
+    for (int bb = 0; bb < 2; ++bb) {
+      const f32x16_t& acc = o[2 * aa + bb];
+      xch[xidx(owner, kl, (gi % kGpk) * 2 + bb)] =
+          f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf;
+    }
   }
   __syncthreads();
   const bool direct = (nsplit == 1);
@@ -540,12 +598,13 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 #pragma unroll
     for (int src = 0; src < KL; ++src) {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+      for (int bb = 0; bb < 2; ++bb) {
+        const f32x16_t& acc = o[2 * aa + bb];
+        const f32x4_t val = (src == kl) ? f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf
+                                        : xch[xidx(kl, src, gl * 2 + bb)];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float val = (src == kl) ? o[2 * aa + bb][4 * ii + k] * asf : xch[xidx(kl, src, gl * 8 + bb * 4 + k)];
-          o8s[gl][2 * k + bb] += val;
-        }
+        for (int k = 0; k < 4; ++k) o8s[gl][2 * k + bb] += val[k];
+      }
     }
   }
   float* stage = reinterpret_cast<float*>(body);  // [kRows][kStageStride], over the exchange area
@@ -592,59 +651,115 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
     }
   }
 
-  // ---- in-kernel merge of the pair's splits (grids that fit on the chip at once). A work
-  // group waits for the other splits only when all of them have started, i.e. are resident
-  // and will finish without needing this CU; the last split to finish always takes every
-  // output slice nobody has claimed, so waiting is never needed for completion. The last
-  // work group to leave returns the counters to zero for the next call.
+  // ---- in-kernel merge of the pair's splits (grids that fit on the chip at once). The
+  // output is cut into one slice per work group of the pair; a slice is merged by whoever
+  // sets its claim bit first. A work group waits for the other splits only when all of them
+  // have started, i.e. are resident and will finish without needing this CU; it then claims
+  // its own slice (finish ticket f) and requests the partials in the same round trip. The
+  // last work group to finish merges its own slice and then claims every other slice at
+  // once, so waiting is never needed for completion and every output quad is written exactly
+  // once. The last work group to leave returns the counters to zero for the next call.
   if (fused) {
-    // Roles: the last work group to finish (finish ticket ns - 1) claims slices until none is
-    // left; a work group that saw every split started waits (bounded) for the others and then
-    // merges the one slice it claims; any other leaves at once. Every slice index is claimed
-    // exactly once, and the last one takes whatever nobody else claimed, so every output quad
-    // is written once and no wait is needed for completion.
-    __shared__ int sh_role, sh_slice;
+    __shared__ int sh_role, sh_f, sh_claim;
+    __shared__ uint32_t sh_won[8];
     const int quads = GM * 32;
     const int per = max((quads + group_wgs - 1) / group_wgs, (quads + 255) / 256);
-    const int nslices = (quads + per - 1) / per;
+    const int nslices = (quads + per - 1) / per;  // <= group_wgs, <= 256
+    const int nwords = (nslices + 31) / 32;
+    const bool fast = nsplit <= kFastSplits;
+    const uint32_t ns = (uint32_t)group_wgs;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's coherent partial stores are done
     __syncthreads();                                   // ... and every other thread's
     if (threadIdx.x == 0) {
-      const uint32_t ns = (uint32_t)group_wgs;
-      const uint32_t f = __hip_atomic_fetch_add(&ctl[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int role = (f == ns - 1) ? 2 : 0;  // 0: leave, 1: merge one slice, 2: merge until none is left
-      if (!role && __hip_atomic_load(&ctl[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
+      const uint32_t f = __hip_atomic_fetch_add(&ctl[kCtlFinished], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t started = __hip_atomic_load(&ctl[kCtlStarted], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int role = (f == ns - 1) ? 2 : 0;  // 0: leave, 1: merge the own slice if still unclaimed, 2: last
+      if (!role && started == ns) {
         for (int it = 0; it < kSpinLimit; ++it) {
-          if (__hip_atomic_load(&ctl[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
+          if (__hip_atomic_load(&ctl[kCtlFinished], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns) {
             role = 1;
             break;
           }
           __builtin_amdgcn_s_sleep(4);
         }
       }
-      // the merge reads the partials with coherent loads issued after this point
-      sh_slice = role ? (int)__hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : nslices;
       sh_role = role;
+      sh_f = (int)f;
     }
     __syncthreads();
-    const int role = sh_role;
-    int slice = sh_slice;
-    __syncthreads();
-    while (role != 0 && slice < nslices) {
-      merge_slice<S::kThreads>(a, b, g, nsplit, slice * per, min(per, quads - slice * per), vsc,
-                               reinterpret_cast<float*>(body));
-      if (role == 1) break;
-      if (threadIdx.x == 0)
-        sh_slice = (int)__hip_atomic_fetch_add(&ctl[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      slice = sh_slice;
-      __syncthreads();
+    const int role = sh_role, f = sh_f;
+    // merges slice k; claimed says whether this group owns it (read after the loads are in flight)
+    auto merge_own = [&](int k, bool claim) {
+      const int q0 = k * per, cnt = min(per, quads - q0);
+      const int t = threadIdx.x;
+      if (fast) {
+        // a slice can hold more quads than the group has threads (few work groups per pair)
+        for (int t0 = 0; t0 < cnt; t0 += S::kThreads) {
+          const int tq = t0 + t;
+          QuadLoads x;
+          if (tq < cnt) quad_issue(a, b, g, nsplit, q0 + tq, x);
+          if (claim && t0 == 0) {
+            if (t == 0) {
+              const uint32_t bit = 1u << (k & 31);
+              const uint32_t old =
+                  __hip_atomic_fetch_or(&ctl[kCtlClaim + (k >> 5)], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              sh_claim = (old & bit) == 0;
+            }
+            __syncthreads();
+            if (!sh_claim) break;  // uniform: the last finisher took the slice
+          }
+          if (tq < cnt) quad_finish(a, b, g, nsplit, q0 + tq, x, vsc);
+        }
+      } else {
+        if (claim) {
+          if (t == 0) {
+            const uint32_t bit = 1u << (k & 31);
+            const uint32_t old =
+                __hip_atomic_fetch_or(&ctl[kCtlClaim + (k >> 5)], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sh_claim = (old & bit) == 0;
+          }
+          __syncthreads();
+        }
+        if (!claim || sh_claim) merge_slice<S::kThreads>(a, b, g, nsplit, q0, cnt, vsc, reinterpret_cast<float*>(body));
+      }
+    };
+    // one merge site: the own slice first, then (last finisher) every slice won in the batch claim
+    int k = (role != 0 && f < nslices) ? f : -1;
+    bool claim = role == 1, batch = role == 2;
+    int wd = 0;
+    uint32_t won = 0u;
+    for (;;) {
+      if (k >= 0) merge_own(k, claim);
+      if (batch) {
+        batch = false;
+        claim = false;
+        if ((int)threadIdx.x < nwords) {
+          const int w0 = 32 * threadIdx.x;
+          const int nb = min(32, nslices - w0);
+          uint32_t mask = nb >= 32 ? ~0u : ((1u << nb) - 1u);
+          if (f >= w0 && f < w0 + 32) mask &= ~(1u << (f - w0));
+          const uint32_t old =
+              __hip_atomic_fetch_or(&ctl[kCtlClaim + threadIdx.x], mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sh_won[threadIdx.x] = mask & ~old;
+        }
+        __syncthreads();
+        won = role == 2 ? sh_won[0] : 0u;
+      } else if (role != 2) {
+        break;
+      }
+      while (won == 0u && role == 2 && ++wd < nwords) won = sh_won[wd];
+      if (won == 0u) break;
+      k = 32 * wd + __builtin_ctz(won);
+      won &= won - 1u;
     }
     if (threadIdx.x == 0) {
-      const uint32_t e = __hip_atomic_fetch_add(&ctl[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (e == (uint32_t)group_wgs - 1) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) __hip_atomic_store(&ctl[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t e = __hip_atomic_fetch_add(&ctl[kCtlExited], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (e == ns - 1) {
+        __hip_atomic_store(&ctl[kCtlStarted], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl[kCtlFinished], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&ctl[kCtlExited], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int wd = 0; wd < nwords; ++wd)
+          __hip_atomic_store(&ctl[kCtlClaim + wd], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
