@@ -57,6 +57,11 @@ def algorithmic_bytes(context, q_len, hq, hkv, block_size, elem):
     return kv, q + out + meta
 
 
+def insert_bytes(q_len, hkv, elem):
+    """BF16 K and V of the new tokens in, the cache's bytes out."""
+    return q_len * hkv * 128 * 2 * (2 + elem)
+
+
 def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
     import torch
     from fp8_kv_paged_amd import fkv, synth
@@ -77,9 +82,38 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
         layers.append(c)
     torch.cuda.synchronize()
 
+    fused_ok = cache_dtype == "fp8_e4m3fn" and args.layout in (0, 5)
+    if fused_ok:
+        base.stage_new_tokens()
+        for c in layers[1:]:
+            c.new_k, c.new_v = base.new_k, base.new_v
+    torch.cuda.synchronize()
+
     stream = torch.cuda.Stream()
+    mean = lambda xs: sum(xs) / len(xs)
+    med = lambda xs: sorted(xs)[len(xs) // 2]
     fkv.reset_counters()
+    res = dict(kv_bytes=kv_bytes, other_bytes=other, copies=copies, working_set=copies * kv_bytes,
+               plan_ws=base.workspace.numel(), fused_insert=fused_ok)
     with torch.cuda.stream(stream):
+        # the decode step as one launch: the new tokens' insert fused into the attention call
+        if fused_ok:
+            for i in range(warmup):
+                layers[i % copies].insert_decode(stream)
+            stream.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                e0, e1 = ev[i]
+                e0.record(stream)
+                layers[(warmup + i) % copies].insert_decode(stream)
+                e1.record(stream)
+            stream.synchronize()
+            res["fused_wall_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
+            f_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+            res["fused_ms"], res["fused_ms_median"] = mean(f_ms), med(f_ms)
+        # the same step as two launches: insert, then decode
         for i in range(warmup):
             L = layers[i % copies]
             L.insert_step(stream)
@@ -99,19 +133,18 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
             e2.record(stream)
         stream.synchronize()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        res["wall_ms_per_step"] = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = [ev[i][0].elapsed_time(ev[i][2]) for i in range(steps)]
     ins_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
     dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
     cnt = fkv.get_counters()
     nt = (72 // 8 * args.q_len + 15) // 16
-    assert cnt["decode_split"][0 if cache_dtype == "fp8_e4m3fn" else 1][nt - 1] == steps + warmup, cnt
-    mean = lambda xs: sum(xs) / len(xs)
-    med = lambda xs: sorted(xs)[len(xs) // 2]
-    return dict(kv_bytes=kv_bytes, other_bytes=other, copies=copies, working_set=copies * kv_bytes,
-                wall_ms_per_step=wall * 1e3 / steps, step_ms=mean(step_ms), insert_ms=mean(ins_ms),
-                decode_ms=mean(dec_ms), decode_ms_median=med(dec_ms), plan_ws=base.workspace.numel(),
-                combine=cnt["decode_combine_launches"] > 0, fused=cnt["decode_combine_launches"] == 0)
+    calls = (steps + warmup) * (2 if fused_ok else 1)
+    assert cnt["decode_split"][0 if cache_dtype == "fp8_e4m3fn" else 1][nt - 1] == calls, cnt
+    assert cnt["insert_decode_launches"] == (steps + warmup if fused_ok else 0), cnt
+    res.update(step_ms=mean(step_ms), insert_ms=mean(ins_ms), decode_ms=mean(dec_ms), decode_ms_median=med(dec_ms),
+               combine=cnt["decode_combine_launches"] > 0, fused=cnt["decode_combine_launches"] == 0)
+    return res
 
 
 def cpu_baseline(seconds):
@@ -197,8 +230,20 @@ def main():
         return
     r = run_gpu(args, args.context, args.block_size, args.cache_dtype, args.steps, args.warmup)
     kv = r["kv_bytes"]
-    value = kv / (r["step_ms"] * 1e-3) / 1e9
-    dec_gbs = (kv + r["other_bytes"]) / (r["decode_ms"] * 1e-3) / 1e9
+    ins_bytes = insert_bytes(args.q_len, 8, 1 if args.cache_dtype == "fp8_e4m3fn" else 2)
+    if r["fused_insert"]:
+        # one launch per step: the roofline covers the whole step (decode and insert bytes)
+        step_ms = r["fused_ms"]
+        alg = kv + r["other_bytes"] + ins_bytes
+        kernel = "decode_m32_kernel (insert fused into decode, one launch per step)"
+        kernel_ms = r["fused_ms"]
+    else:
+        step_ms = r["step_ms"]
+        alg = kv + r["other_bytes"]
+        kernel = f"{DECODE_KERNELS[args.layout]}" + ("" if r["fused"] else " + decode_combine_kernel") + " (one decode call)"
+        kernel_ms = r["decode_ms"]
+    value = kv / (step_ms * 1e-3) / 1e9
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
     src = source_hash()
     cfg_name = f"c3_m{args.q_len}_{args.context}_p{args.block_size}_{args.cache_dtype}"
     line = {
@@ -208,29 +253,31 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["step_ms"], 5),
+        "ms_per_step": round(step_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3fn KV, bf16 Q, f32 accumulate" if args.cache_dtype == "fp8_e4m3fn" else "bf16",
         "data": "synthetic",
         "config": {"workload": f"full layer, 72 Q / 8 KV heads, head 128, context {args.context}, M={args.q_len} "
-                               f"causal, global, page {args.block_size}, {args.cache_dtype} cache",
+                               f"causal, global, page {args.block_size}, {args.cache_dtype} cache; one step = insert "
+                               f"the {args.q_len} new tokens + decode attention",
                    "context": args.context, "q_len": args.q_len, "block_size": args.block_size,
                    "layer_copies": r["copies"], "working_set_bytes": r["working_set"], "split_tiles": args.split_tiles},
-        "us_per_layer": round(r["step_ms"] * 1e3, 3),
+        "us_per_layer": round(step_ms * 1e3, 3),
+        "step_launches": 1 if r["fused_insert"] else 2,
+        "separate_launches": {"step_us": round(r["step_ms"] * 1e3, 3), "insert_us": round(r["insert_ms"] * 1e3, 3),
+                              "decode_us": round(r["decode_ms"] * 1e3, 3),
+                              "decode_us_median": round(r["decode_ms_median"] * 1e3, 3)},
         "decode_us_per_layer": round(r["decode_ms"] * 1e3, 3),
-        "decode_us_median": round(r["decode_ms_median"] * 1e3, 3),
-        "insert_us": round(r["insert_ms"] * 1e3, 3),
         "kv_read_pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "decode_kv_gbs": round(kv / (r["decode_ms"] * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(src, cfg_name),
-                     "kernel": f"{DECODE_KERNELS[args.layout]}" + ("" if r["fused"] else " + decode_combine_kernel")
-                               + " (one decode call)",
-                     "algorithmic_bytes": kv + r["other_bytes"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(src, cfg_name),
+                     "kernel": kernel, "algorithmic_bytes": alg},
         "source_hash": src,
     }
+    if r["fused_insert"]:
+        line["fused_us_median"] = round(r["fused_ms_median"] * 1e3, 3)
     if args.ab:
         extra = {}
         for ctx, bs in ((8192, 32), (8192, 64), (32768, 32), (32768, 64)):
@@ -238,6 +285,8 @@ def main():
             extra[f"{ctx}_p{bs}"] = {"decode_us": round(rr["decode_ms"] * 1e3, 3),
                                      "decode_kv_gbs": round(rr["kv_bytes"] / (rr["decode_ms"] * 1e-3) / 1e9, 1),
                                      "insert_us": round(rr["insert_ms"] * 1e3, 3)}
+            if rr["fused_insert"]:
+                extra[f"{ctx}_p{bs}"]["fused_step_us"] = round(rr["fused_ms"] * 1e3, 3)
         line["ab"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -18,6 +18,7 @@ constexpr uint64_t kAlign = 256;
 std::atomic<uint64_t> g_insert[2];
 std::atomic<uint64_t> g_split[2][9];
 std::atomic<uint64_t> g_combine;
+std::atomic<uint64_t> g_insert_decode;
 std::atomic<uint64_t> g_rejected;
 
 int reject(int code) {
@@ -241,14 +242,18 @@ int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* de
   return FKV_OK;
 }
 
-int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
-                    const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
-                    const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q, const uint16_t* k_new,
+                       const uint16_t* v_new, const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                       const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   fkv::DecodePlan p;
   int rc = plan_decode(cache, desc, &p);
   if (rc) return reject(rc);
-  if (desc->num_seqs == 0) return FKV_OK;
+  const bool fused_insert = k_new != nullptr;
   const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
+  // the fused insert exists in the 32-row kernel only (FP8 cache, layout 5 or automatic)
+  if (fused_insert && (!fp8 || fkv::split_shape(p.nt, p.layout, fp8).groups_per_cu != -2)) return reject(FKV_EUNSUPPORTED);
+  if (desc->num_seqs == 0) return FKV_OK;
+  if (fused_insert && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return reject(FKV_EINVAL);
   if (!q || !block_table || !seq_lens || !out) return reject(FKV_EINVAL);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
     return reject(FKV_EINVAL);
@@ -260,6 +265,8 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
   a.v_pool = static_cast<const uint8_t*>(cache->v_pool);
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = fused_insert ? v_new : nullptr;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.k_scale = k_scale;
@@ -293,7 +300,24 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   if (e != hipSuccess) return reject(FKV_EHIP);
   g_split[fp8 ? 0 : 1][p.nt - 1].fetch_add(1, std::memory_order_relaxed);
   if (combined) g_combine.fetch_add(1, std::memory_order_relaxed);
+  if (fused_insert) g_insert_decode.fetch_add(1, std::memory_order_relaxed);
   return FKV_OK;
+}
+
+int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                    const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                    const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(cache, desc, q, nullptr, nullptr, block_table, seq_lens, k_scale, v_scale, out, workspace,
+                     workspace_bytes, stream);
+}
+
+int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q, const uint16_t* k_new,
+                      const uint16_t* v_new, const int32_t* block_table, const int32_t* seq_lens,
+                      const float* k_scale, const float* v_scale, void* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!k_new || !v_new) return reject(FKV_EINVAL);
+  return decode_call(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, v_scale, out, workspace,
+                     workspace_bytes, stream);
 }
 
 const char* fkv_status_string(int status) {
@@ -315,6 +339,7 @@ int fkv_get_counters(fkv_counters* out) {
     for (int j = 0; j < 9; ++j) out->decode_split[i][j] = g_split[i][j].load(std::memory_order_relaxed);
   }
   out->decode_combine_launches = g_combine.load(std::memory_order_relaxed);
+  out->insert_decode_launches = g_insert_decode.load(std::memory_order_relaxed);
   out->rejected_calls = g_rejected.load(std::memory_order_relaxed);
   return FKV_OK;
 }
@@ -325,6 +350,7 @@ int fkv_reset_counters(void) {
     for (int j = 0; j < 9; ++j) g_split[i][j].store(0);
   }
   g_combine.store(0);
+  g_insert_decode.store(0);
   g_rejected.store(0);
   return FKV_OK;
 }

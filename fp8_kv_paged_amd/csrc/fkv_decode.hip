@@ -223,8 +223,8 @@ __device__ __forceinline__ void softmax_pv_tile(const DecodeArgs& a, const Split
         for (int i = 0; i < 4; ++i) p[tt][i] = __builtin_amdgcn_exp2f(fmaf(sacc[tt][t][i], C, -ms));
       // Four separate packed words: with the words read back out of one vector the
       // dot products were emitted on the first word four times.
-      const uint32_t h0 = pack_f16_rtz(p[0][0], p[0][1]), h1 = pack_f16_rtz(p[0][2], p[0][3]);
-      const uint32_t h2 = pack_f16_rtz(p[1][0], p[1][1]), h3 = pack_f16_rtz(p[1][2], p[1][3]);
+      const uint32_t h0 = pack_f16(p[0][0], p[0][1]), h1 = pack_f16(p[0][2], p[0][3]);
+      const uint32_t h2 = pack_f16(p[1][0], p[1][1]), h3 = pack_f16(p[1][2], p[1][3]);
       P[t] = __builtin_bit_cast(f16x8_t, u32x4_t{h0, h1, h2, h3});
       // the row sum uses the same rounded probabilities the PV product sees
       const f16x2_t one2 = __builtin_bit_cast(f16x2_t, ones);

@@ -37,6 +37,22 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | (r - (120u << 3));                   // rebias exponent 127 -> 7
 }
 
+// Eight BF16 values (16 bytes; element j in the high or low half of word j/2) -> eight
+// E4M3FN codes: code j = e4m3_encode(fp32(x_j) / scale) with one correctly rounded fp32
+// division, in byte j%4 of lo (j < 4) or hi (j >= 4). Cache insertion, standalone or fused
+// into decode, stores exactly these bytes.
+__device__ __forceinline__ void e4m3_encode8(const u32x4_t& in, float scale, uint32_t& lo, uint32_t& hi) {
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = in[j >> 1];
+    const float x = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    c[j >> 2] |= e4m3_encode(__fdiv_rn(x, scale)) << (8 * (j & 3));
+  }
+  lo = c[0];
+  hi = c[1];
+}
+
 // ---- fp8 -> bf16 / f16 (hardware, exact for every E4M3FN code) -------------------------
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -81,8 +97,10 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-__device__ __forceinline__ uint32_t pack_f16_rtz(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+// Two fp32 values -> packed f16, round to nearest even (one v_cvt_pk_f16_f32 on gfx950):
+// the attention weights fed to the f16 P.V product and to the row sums.
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)a, (_Float16)b});
 }
 
 }  // namespace fkv

@@ -14,10 +14,6 @@
 
 namespace fkv {
 
-__device__ __forceinline__ float bf16_word_to_f32(uint32_t w, int hi) {
-  return __uint_as_float(hi ? (w & 0xFFFF0000u) : (w << 16));
-}
-
 template <bool kFp8>
 __global__ __launch_bounds__(256) void cache_insert_kernel(InsertArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -39,19 +35,12 @@ __global__ __launch_bounds__(256) void cache_insert_kernel(InsertArgs a) {
   const u32x4_t vin = *reinterpret_cast<const u32x4_t*>(a.v + th * kHeadDim + c * 8);
 
   if constexpr (kFp8) {
-    const float ks = *a.k_scale;
-    const float vs = *a.v_scale;
-    uint32_t kc[2] = {0u, 0u};
+    uint32_t kc[2], vc[2];
+    e4m3_encode8(kin, *a.k_scale, kc[0], kc[1]);
+    e4m3_encode8(vin, *a.v_scale, vc[0], vc[1]);
     uint8_t* vp = static_cast<uint8_t*>(a.v_pool) + v_off;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float kx = bf16_word_to_f32(kin[j >> 1], j & 1);
-      const float vx = bf16_word_to_f32(vin[j >> 1], j & 1);
-      const uint32_t kcode = e4m3_encode(__fdiv_rn(kx, ks));
-      const uint32_t vcode = e4m3_encode(__fdiv_rn(vx, vs));
-      kc[j >> 2] |= kcode << (8 * (j & 3));
-      vp[j * 8] = (uint8_t)vcode;
-    }
+    for (int j = 0; j < 8; ++j) vp[j * 8] = (uint8_t)(vc[j >> 2] >> (8 * (j & 3)));
     *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.k_pool) + k_off) = u32x2_t{kc[0], kc[1]};
   } else {
     *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.k_pool) + k_off) = kin;

@@ -34,7 +34,7 @@ struct DecodePlan {
   int max_splits;      // grid x
   size_t ws_o_bytes;   // fp32 partial outputs
   size_t ws_ml_bytes;  // fp32 (m, l) per partial row
-  size_t ws_ctl_bytes; // uint32 control counters of the in-kernel split merge (4 per pair)
+  size_t ws_ctl_bytes; // in-kernel split merge: 256 bytes of counters and claim bits per pair
   int fused_combine;   // layout 5 with the whole grid resident: splits merged inside the kernel
   int xcd_pairs;       // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   size_t ws_bytes;     // total, 256-byte aligned pieces
@@ -44,6 +44,8 @@ struct DecodeArgs {
   const uint8_t* k_pool;
   const uint8_t* v_pool;
   const uint16_t* q;
+  const uint16_t* k_new;  // fused insert (32-row kernel): BF16 [num_seqs][q_len][num_kv_heads][128], or null
+  const uint16_t* v_new;
   const int32_t* block_table;
   const int32_t* seq_lens;
   const float* k_scale;
@@ -51,7 +53,7 @@ struct DecodeArgs {
   float* out;
   float* ws_o;
   float* ws_ml;
-  uint32_t* ws_ctl;      // 4 counters per (sequence, KV head): started, finished, claimed, exited
+  uint32_t* ws_ctl;      // 64 words per (sequence, KV head): merge counters and claim bits
   int32_t num_seqs, num_q_heads, num_kv_heads, group, q_len, block_size, max_blocks, num_blocks;
   int32_t window_left, tiles_per_split, max_splits, max_seq_len, rows_pad;
   int32_t row_groups;  // row-group kernel: groups of 16*ntw packed rows

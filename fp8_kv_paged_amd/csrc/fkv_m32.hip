@@ -18,7 +18,7 @@
 //     in the order the MFMA operands want it, so the LDS reads are lane-contiguous.
 //   * S^T = K Q^T on MFMA 32x32x16 bf16 (fp8 -> bf16 exact), online softmax in the log2
 //     domain against a lazily raised per-row reference, O^T += V^T P^T on MFMA 32x32x16
-//     f16 (fp8 -> f16 exact, P rounded to f16). The S^T products of tile i+1 are issued in
+//     f16 (fp8 -> f16 exact, P rounded to the nearest f16). The S^T products of tile i+1 are issued in
 //     the same block as the probabilities of tile i, so MFMA and VALU work interleave.
 //   * After the loop the KL key lanes of a row tile merge through LDS in a fixed order
 //     and the group writes final rows (one split) or an fp32 partial (m, l, O) that
@@ -65,7 +65,8 @@ struct M32Shape {
   static_assert((kDepth - 2) * kPerWave <= 63, "vmcnt range");
   static_assert(KL * kChunks % kWaves == 0, "DMA chunks split evenly over the waves");
   static_assert(8 % KL == 0, "output groups split evenly over the key lanes");
-  static_assert(256 + kBody + 2 * KL * RT * 32 * 4 <= 160 * 1024, "LDS budget of one CU");
+  static constexpr int kInsLds = 16 * kHeadDim + kHeadDim * 64;  // fused insert: K and V codes
+  static_assert(256 + kBody + 2 * KL * RT * 32 * 4 + kInsLds <= 160 * 1024, "LDS budget of one CU");
 };
 
 // O^T += V^T P^T. The accumulators stay in VGPRs (MFMA VGPR form): pinning them to AGPRs
@@ -348,12 +349,27 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 #pragma unroll
     for (int c = 0; c < 8; ++c) qraw[c] = u32x4_t{0u, 0u, 0u, 0u};
   }
-  // Complete the page-table and Q loads through an asm that redefines their registers:
-  // later reads carry no load dependence, so the compiler adds no wait on the DMAs below,
-  // whose counts the loop relies on.
+  // Fused insert: every group requests the q_len new tokens' K and V of its KV head with Q
+  // (thread t < 16 M: K of token t / 16, dims 8 (t % 16) .. +7; the next 16 M threads: V);
+  // only the groups whose split holds the new positions use them.
+  const bool fuse_ins = a.k_new != nullptr;
+  const int ci = (int)threadIdx.x < 16 * M ? (int)threadIdx.x : (int)threadIdx.x - 16 * M;  // chunk of K or V
+  const bool ins_v_chunk = (int)threadIdx.x >= 16 * M;
+  const bool ins_chunk = fuse_ins && (int)threadIdx.x < 32 * M;
+  u32x4_t nraw{0u, 0u, 0u, 0u};
+  float vs_ins = 1.0f;
+  if (ins_chunk) {
+    const uint16_t* src = (ins_v_chunk ? a.v_new : a.k_new) +
+                          (((int64_t)b * M + (ci >> 4)) * a.num_kv_heads + g) * kHeadDim + 8 * (ci & 15);
+    nraw = *reinterpret_cast<const u32x4_t*>(src);
+    vs_ins = *a.v_scale;
+  }
+  // Complete the page-table, Q and new-token loads through an asm that redefines their
+  // registers: later reads carry no load dependence, so the compiler adds no wait on the
+  // DMAs below, whose counts the loop relies on.
   asm volatile("s_waitcnt vmcnt(0)"
                : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]), "+v"(qraw[4]),
-                 "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7])::"memory");
+                 "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]), "+v"(nraw), "+v"(vs_ins)::"memory");
   const float C = a.softmax_scale * ks * kLog2e;
   auto block_of = [&](int tile) -> int {
     const int e = (tile >> bshift) - lb0;
@@ -460,7 +476,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 #pragma unroll
     for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(sc[v], C, -m_ref));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) hw[k] = pack_f16_rtz(p[2 * k], p[2 * k + 1]);
+    for (int k = 0; k < 8; ++k) hw[k] = pack_f16(p[2 * k], p[2 * k + 1]);
     // the row sum uses the same rounded probabilities the PV product sees
     const f16x2_t one2 = __builtin_bit_cast(f16x2_t, 0x3C003C00u);
     float l = 0.f;
@@ -500,6 +516,87 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
       }
   };
 
+  // ---- fused insert ("Laguna S 2.1 INT4 -- calibrated FP8 KV on Intel B70", section "Initial
+  // optimization order": scaled E4M3 insertion; its fusion into the attention call is the
+  // next step named there). New token i sits at position L - M + i. The groups whose split
+  // holds new positions encode them into LDS; row group 0 of the split also stores them
+  // into the pool. The ring's copy of a tile holding new keys is patched from LDS after it
+  // is read, so the DMAs need no ordering against the pool stores (whose bytes they may or
+  // may not see).
+  __shared__ __align__(16) unsigned char ins_k[16 * kHeadDim];  // [token][dim]
+  __shared__ __align__(16) unsigned char ins_v[kHeadDim * 64];  // [dim][position - 32 tn0]
+  const int pn0 = max(0, L - M);  // first new position
+  const int tn0 = pn0 / kTile;    // first tile holding a new key
+  const bool ins = fuse_ins && L > pn0 && pn0 < te * kTile && L > tb * kTile;  // uniform
+  if (ins) {
+    const int p = L - M + (ci >> 4);  // this thread's token position
+    // physical block of p from the split's page-table window (lanes hold entries lb0 + lane
+    // and lb0 + 64 + lane); positions outside the split are not stored
+    const int e = min(max((p >> (5 + bshift)) - lb0, 0), 127);
+    const int blo = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_lo);
+    const int bhi = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_hi);
+    const int blk = e < 64 ? blo : bhi;
+    if (ins_chunk && p >= 0) {
+      uint32_t c0, c1;
+      e4m3_encode8(nraw, ins_v_chunk ? vs_ins : ks, c0, c1);
+      const int d0 = 8 * (ci & 15);
+      if (!ins_v_chunk) {
+        *reinterpret_cast<u32x2_t*>(ins_k + (ci >> 4) * kHeadDim + d0) = u32x2_t{c0, c1};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ins_v[(d0 + j) * 64 + (p - kTile * tn0)] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
+      }
+      if (rg == 0 && p >= tb * kTile && p < te * kTile && (unsigned)blk < (unsigned)a.num_blocks) {
+        const int off = p & (a.block_size - 1);
+        const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes;
+        if (!ins_v_chunk) {
+          *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) = u32x2_t{c0, c1};
+        } else {
+          uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + slab + (off >> 3) * 1024 + d0 * 8 + (off & 7);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vp[j * 8] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
+        }
+      }
+    }
+    // the codes are in LDS before any tile is read; the pool stores stay in flight (they are
+    // older than every DMA, so the per-step DMA waits still count correctly)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  // replaces the ring's bytes of new keys in a tile's registers by their codes
+  auto patch = [&](int tile, TileRegs32<true>& x) {
+    const int kt = tile * kTile;
+    const int pk = kt + key_of_row(n);  // key of this lane's K operand row
+    if (pk >= pn0 && pk < L) {
+      const unsigned char* src = ins_k + (pk - (L - M)) * kHeadDim + 16 * hh;
+      x.k[0][0] = *reinterpret_cast<const u32x4_t*>(src);
+      x.k[0][1] = *reinterpret_cast<const u32x4_t*>(src + 32);
+      x.k[1][0] = *reinterpret_cast<const u32x4_t*>(src + 64);
+      x.k[1][1] = *reinterpret_cast<const u32x4_t*>(src + 96);
+    }
+#pragma unroll
+    for (int cp = 0; cp < 2; ++cp) {
+      const int k0 = kt + 16 * cp + 8 * hh;  // keys k0 .. k0 + 7 of dims 64 aa + 2n (+1)
+      const int e0 = min(8, max(0, pn0 - k0)), e1 = min(8, max(0, L - k0));
+      if (e0 < e1) {
+        const uint64_t sel = (e1 >= 8 ? ~0ull : ((1ull << (8 * e1)) - 1)) & ~((1ull << (8 * e0)) - 1);
+        const int col = k0 - kTile * tn0;
+#pragma unroll
+        for (int aa = 0; aa < 2; ++aa) {
+          u32x4_t& xv = x.v[2 * cp + aa];
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            const uint64_t cw = *reinterpret_cast<const uint64_t*>(ins_v + (64 * aa + 2 * n + bb) * 64 + col);
+            const uint64_t rw = ((uint64_t)xv[2 * bb + 1] << 32) | xv[2 * bb];
+            const uint64_t mw = (rw & ~sel) | (cw & sel);
+            xv[2 * bb] = (uint32_t)mw;
+            xv[2 * bb + 1] = (uint32_t)(mw >> 32);
+          }
+        }
+      }
+    }
+  };
+  auto has_new = [&](int tile) -> bool { return ins && tile * kTile + kTile > pn0 && tile * kTile < L; };
+
   // ---- the pipeline. kDepth steps are in flight; one barrier per step publishes a step
   // and certifies that every wave has read the slot the next request overwrites. A wave
   // computes S^T of tile i+1 in the same block as the probabilities of tile i, so MFMA and
@@ -516,6 +613,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   f32x16_t sa, sb;
   if (nfull > 0) {
     read_slot<true>(slot0, xa);
+    if (has_new(tb + kl)) patch(tb + kl, xa);
     qk(xa, sa);
   }
   for (int i = 0; i < nsteps; ++i) {
@@ -531,6 +629,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
     float lt;
     if (i + 1 < nfull) {
       read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xb);
+      if (has_new(tile + KL)) patch(tile + KL, xb);
       // S^T of the next tile interleaved with this tile's probabilities
       qk(xb, sb);
       lt = probs(sa, hw);

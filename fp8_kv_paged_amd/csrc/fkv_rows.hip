@@ -325,8 +325,8 @@ void decode_rows_kernel(DecodeArgs a) {
           for (int e = 0; e < 4; ++e) p[tt][e] = __builtin_amdgcn_exp2f(fmaf(x.s[tt][t][e], C, -ms));
         // four separate words: read back out of one vector, the dot products were once
         // emitted on the first word four times
-        const uint32_t h0 = pack_f16_rtz(p[0][0], p[0][1]), h1 = pack_f16_rtz(p[0][2], p[0][3]);
-        const uint32_t h2 = pack_f16_rtz(p[1][0], p[1][1]), h3 = pack_f16_rtz(p[1][2], p[1][3]);
+        const uint32_t h0 = pack_f16(p[0][0], p[0][1]), h1 = pack_f16(p[0][2], p[0][3]);
+        const uint32_t h2 = pack_f16(p[1][0], p[1][1]), h3 = pack_f16(p[1][2], p[1][3]);
         P[t] = __builtin_bit_cast(f16x8_t, u32x4_t{h0, h1, h2, h3});
         // the row sum uses the same rounded probabilities the PV product sees
         float l = lsum[t];

@@ -287,8 +287,8 @@ __global__ __launch_bounds__(kWideThreads, 1) void decode_wide_kernel(DecodeArgs
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) p[tt][e] = __builtin_amdgcn_exp2f(fmaf(sc[tt][t][e], C, -m_ref[t]));
-        const uint32_t h0 = pack_f16_rtz(p[0][0], p[0][1]), h1 = pack_f16_rtz(p[0][2], p[0][3]);
-        const uint32_t h2 = pack_f16_rtz(p[1][0], p[1][1]), h3 = pack_f16_rtz(p[1][2], p[1][3]);
+        const uint32_t h0 = pack_f16(p[0][0], p[0][1]), h1 = pack_f16(p[0][2], p[0][3]);
+        const uint32_t h2 = pack_f16(p[1][0], p[1][1]), h3 = pack_f16(p[1][2], p[1][3]);
         P[t] = __builtin_bit_cast(f16x8_t, u32x4_t{h0, h1, h2, h3});
         // the row sum uses the same rounded probabilities the PV product sees
         const f16x2_t one2 = __builtin_bit_cast(f16x2_t, 0x3C003C00u);

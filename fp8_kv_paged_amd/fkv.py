@@ -1,7 +1,8 @@
 """Python binding of libfkv.so: the C entry points of include/fkv.h, marshalled with ctypes.
 
 Names follow the C ABI without its `fkv_` prefix (cache_bytes, init_cache, insert,
-decode_workspace_bytes, decode_attn, status_string, get_counters, reset_counters).
+decode_workspace_bytes, decode_attn, insert_decode, status_string, get_counters,
+reset_counters).
 Every step of the path runs in the HIP library; this module only checks tensor
 placement and passes pointers, sizes and the current HIP stream. There is no
 fallback: if the library is missing, loading raises.
@@ -46,7 +47,8 @@ class DecodeDesc(ctypes.Structure):
 
 class Counters(ctypes.Structure):
     _fields_ = [("insert_launches", ctypes.c_uint64 * 2), ("decode_split", (ctypes.c_uint64 * 9) * 2),
-                ("decode_combine_launches", ctypes.c_uint64), ("rejected_calls", ctypes.c_uint64)]
+                ("decode_combine_launches", ctypes.c_uint64), ("rejected_calls", ctypes.c_uint64),
+                ("insert_decode_launches", ctypes.c_uint64)]
 
 
 _lib = None
@@ -66,12 +68,14 @@ def lib():
         L.fkv_decode_workspace_bytes.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), ctypes.POINTER(sz)]
         L.fkv_decode_attn.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
                                       sz, vp]
+        L.fkv_insert_decode.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, sz, vp]
         L.fkv_status_string.argtypes = [ctypes.c_int]
         L.fkv_status_string.restype = ctypes.c_char_p
         L.fkv_get_counters.argtypes = [ctypes.POINTER(Counters)]
         L.fkv_reset_counters.argtypes = []
         for f in ("fkv_cache_bytes", "fkv_init_cache", "fkv_insert", "fkv_decode_workspace_bytes", "fkv_decode_attn",
-                  "fkv_get_counters", "fkv_reset_counters"):
+                  "fkv_insert_decode", "fkv_get_counters", "fkv_reset_counters"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,12 +173,34 @@ def decode_attn(cache, desc, q, block_table, seq_lens, k_scale, v_scale, out, wo
            "fkv_decode_attn")
 
 
+def insert_decode(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, v_scale, out, workspace=None,
+                  stream=None):
+    """fkv_insert_decode: k_new / v_new BF16 [B, M, Hkv, 128] (the M new tokens of each sequence, at
+    positions L-M .. L-1); the other arguments as decode_attn."""
+    B, M, Hq = desc.num_seqs, desc.q_len, desc.num_q_heads
+    if q.numel() != B * M * Hq * HEAD_DIM or out.numel() != B * M * Hq * HEAD_DIM:
+        raise ValueError("q / out do not match the decode descriptor")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.numel() != B * M * cache.desc.num_kv_heads * HEAD_DIM:
+            raise ValueError(f"{name} must hold num_seqs x q_len x num_kv_heads x 128 elements")
+    if block_table.numel() != B * desc.max_blocks_per_seq or seq_lens.numel() != B:
+        raise ValueError("block_table / seq_lens do not match the decode descriptor")
+    ws = _ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().fkv_insert_decode(ctypes.byref(cache), ctypes.byref(desc), _ptr(q, "q", 2), _ptr(k_new, "k_new", 2),
+                                   _ptr(v_new, "v_new", 2), _ptr(block_table, "block_table", 4),
+                                   _ptr(seq_lens, "seq_lens", 4), _ptr(k_scale, "k_scale", 4),
+                                   _ptr(v_scale, "v_scale", 4), _ptr(out, "out", 4), ws, ws_bytes, _stream(stream)),
+           "fkv_insert_decode")
+
+
 def get_counters():
     c = Counters()
     _check(lib().fkv_get_counters(ctypes.byref(c)), "fkv_get_counters")
     return {"insert_launches": list(c.insert_launches),
             "decode_split": [list(r) for r in c.decode_split],
             "decode_combine_launches": c.decode_combine_launches,
+            "insert_decode_launches": c.insert_decode_launches,
             "rejected_calls": c.rejected_calls}
 
 

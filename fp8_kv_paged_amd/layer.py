@@ -45,6 +45,7 @@ class PagedLayer:
         # zero once: the split-merge counters at its end must start at zero (calls leave them so)
         self.workspace = torch.zeros((max(nws, 16),), dtype=torch.uint8, device=device)
         self.step_k = self.step_v = self.step_slots = None
+        self.new_k = self.new_v = None
 
     def set_split_tiles(self, split_tiles):
         self.ddesc.split_tiles = int(split_tiles)
@@ -80,6 +81,27 @@ class PagedLayer:
         self.step_k = to_dev_bits(np.concatenate(ks), self.device)
         self.step_v = to_dev_bits(np.concatenate(vs), self.device)
         self.step_slots = torch.from_numpy(np.concatenate(ss).astype(np.int32)).to(self.device)
+
+    def stage_new_tokens(self):
+        """The q_len new tokens of every sequence as [num_seqs, q_len, Hkv, 128] BF16 (the layout of
+        insert_decode); positions below 0 (seq_len < q_len) are zero rows, which are not stored."""
+        M, H = self.lay.q_len, self.lay.num_kv_heads
+        k = np.zeros((self.lay.num_seqs, M, H, HEAD_DIM), dtype=np.uint16)
+        v = np.zeros_like(k)
+        for b in range(self.lay.num_seqs):
+            L = int(self.lay.seq_lens[b])
+            t0 = max(0, L - M)
+            kb, vb = self.lay.kv_bits(b, t0, L)
+            k[b, M - (L - t0):] = kb.reshape(L - t0, H, HEAD_DIM)
+            v[b, M - (L - t0):] = vb.reshape(L - t0, H, HEAD_DIM)
+        self.new_k = to_dev_bits(k, self.device)
+        self.new_v = to_dev_bits(v, self.device)
+
+    def insert_decode(self, stream=None):
+        """One launch: insert the staged new tokens and decode."""
+        fkv.insert_decode(self.cache, self.ddesc, self.q, self.new_k, self.new_v, self.block_table, self.seq_lens,
+                          self.k_scale, self.v_scale, self.out, self.workspace, stream)
+        return self.out
 
     def insert_step(self, stream=None):
         fkv.insert(self.cache, self.step_k, self.step_v, self.step_slots, self.k_scale, self.v_scale, stream)

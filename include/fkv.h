@@ -203,6 +203,30 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
                     const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
                     const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Cache insertion of the q_len new tokens fused into decode attention: one launch
+ * with the effect of fkv_insert of the new tokens followed by fkv_decode_attn
+ * ([P1] "Initial optimization order": scaled E4M3 insertion, with fusing it into
+ * the neighbouring step named as the next optimization).
+ *
+ *  k_new, v_new  device BF16 [num_seqs][q_len][num_kv_heads][128]: token i of
+ *                sequence b goes to position p = L - q_len + i (L = seq_lens[b],
+ *                which counts the new tokens), i.e. to block block_table[b][p /
+ *                block_size], offset p % block_size. Positions p < 0 and block ids
+ *                outside [0, num_blocks) are skipped, as fkv_insert skips such slots.
+ *  other arguments as fkv_decode_attn (same descriptor, workspace and rules).
+ *
+ * The pool bytes written are those fkv_insert writes for the same tokens, and out is
+ * bitwise equal to fkv_decode_attn's after that insert. The attention reads the new
+ * keys from the codes it computed, not back from the pool, so no ordering between
+ * the two is needed. FP8 cache and layout 0 or 5 only (else FKV_EUNSUPPORTED).
+ * Errors: as fkv_decode_attn, plus FKV_EINVAL for a null or misaligned k_new/v_new.
+ */
+int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                      const uint16_t* k_new, const uint16_t* v_new, const int32_t* block_table,
+                      const int32_t* seq_lens, const float* k_scale, const float* v_scale, void* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* fkv_status_string(int status);
 
@@ -218,6 +242,8 @@ typedef struct fkv_counters {
   uint64_t decode_split[2][9];
   uint64_t decode_combine_launches;
   uint64_t rejected_calls;          /* calls that returned an error            */
+  uint64_t insert_decode_launches;  /* fkv_insert_decode calls (also counted in
+                                       decode_split)                            */
 } fkv_counters;
 
 int fkv_get_counters(fkv_counters* out);

@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     L = fkv.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -145,6 +145,26 @@ def test_calls_fail_closed_without_touching_the_gpu():
     # a tampered handle is rejected
     c.pool_bytes += 1
     assert L.fkv_insert(ctypes.byref(c), dev, dev, dev, 4, dev, dev, None) == fkv.EINVAL
+
+
+def test_insert_decode_fails_closed_without_touching_the_gpu():
+    L = fkv.lib()
+    c = _fake_cache()
+    d = fkv.make_decode_desc(1, 12, 18, 8, 256)
+    dev = ctypes.c_void_p(0x300000)
+    call = lambda cache, desc, kn, vn, ws=dev, nws=1 << 30: L.fkv_insert_decode(
+        ctypes.byref(cache), ctypes.byref(desc), dev, kn, vn, dev, dev, dev, dev, dev, ws, nws, None)
+    assert call(c, d, None, dev) == fkv.EINVAL                     # no new keys
+    assert call(c, d, dev, None) == fkv.EINVAL                     # no new values
+    assert call(c, d, ctypes.c_void_p(0x300002), dev) == fkv.EINVAL  # misaligned
+    d.layout = 3                                                   # only the 32-row kernel fuses the insert
+    assert call(c, d, dev, dev) == fkv.EUNSUPPORTED
+    d.layout = 5
+    d.split_tiles = 1
+    assert call(c, d, dev, dev, ws=None, nws=0) == fkv.EWORKSPACE
+    c16 = _fake_cache(dt="bf16")
+    assert call(c16, fkv.make_decode_desc(1, 12, 18, 8, 256), dev, dev) == fkv.EUNSUPPORTED
+    assert call(c, fkv.make_decode_desc(0, 12, 18, 8, 256), dev, dev) == fkv.OK  # no sequences: no launch
 
 
 def test_counters_record_rejections():

@@ -1,0 +1,150 @@
+"""GPU parity of the fused insert + decode entry point (fkv_insert_decode): the pool bytes
+it writes equal fkv_insert's for the same tokens, its output equals fkv_decode_attn's
+after that insert bit for bit, and both are checked against the oracle (row-normalised
+error <= 2e-3). Cases put the new tokens across tile, page and split boundaries, below
+position 0 (seq_len < q_len), in sliding windows and in every row-group split."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_kv_paged_amd import fkv, synth
+from fp8_kv_paged_amd.layer import PagedLayer
+from oracle import attention
+
+import parity
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def _reference(lay, b):
+    """Oracle output of sequence b; with seq_len L < q_len the first q_len - L rows sit at
+    negative positions (no visible key: zeros) and the rest are the oracle over q_len = L."""
+    M, L = lay.q_len, int(lay.seq_lens[b])
+    if L >= M:
+        return parity.reference(lay, b)
+    G = lay.num_q_heads // lay.num_kv_heads
+    k, v = parity.logical_kv(lay, b)
+    q = parity.q_f64(lay, b)
+    out = np.zeros(q.shape)
+    for g in range(lay.num_kv_heads):
+        sl = slice(g * G, (g + 1) * G)
+        out[M - L:, sl] = attention.decode_attention(q[M - L:, sl], k[:, g:g + 1], v[:, g:g + 1], L,
+                                                     lay.window_left, lay.softmax_scale)
+    return out
+
+
+def _check(lay, out, label):
+    gpu = out.cpu().numpy()
+    worst = 0.0
+    for b in range(lay.num_seqs):
+        L = int(lay.seq_lens[b])
+        if L < lay.q_len:
+            assert np.all(gpu[b, :lay.q_len - L] == 0.0), (label, b)
+        worst = max(worst, float(parity.row_errors(gpu[b], _reference(lay, b)).max()))
+    print(f"[insert_decode parity] {label}: max row error {worst:.3e}", flush=True)
+    assert worst <= parity.ATTN_TOL, (label, worst)
+
+
+def _fused_vs_separate(lay, label, **kw):
+    fused = PagedLayer(lay, **kw)
+    fused.prefill()
+    fused.stage_new_tokens()
+    sep = PagedLayer(lay, **kw).build()
+    before = fkv.get_counters()["insert_decode_launches"]
+    out_f = fused.insert_decode().clone()
+    out_s = sep.decode().clone()
+    torch.cuda.synchronize()
+    assert fkv.get_counters()["insert_decode_launches"] == before + 1
+    assert torch.equal(fused.k_pool, sep.k_pool), f"{label}: K pool differs from fkv_insert's"
+    assert torch.equal(fused.v_pool, sep.v_pool), f"{label}: V pool differs from fkv_insert's"
+    assert torch.equal(out_f, out_s), f"{label}: output differs from insert + decode"
+    _check(lay, out_f, label)
+    return fused
+
+
+def _workloads():
+    yield "c1", synth.c1_layer
+    yield "c2", synth.c2_layer
+    yield "c3_8k_p32", lambda: synth.c3_layer(8192, 32)
+    yield "c3_8k_p64", lambda: synth.c3_layer(8192, 64)
+    yield "c3_32k_p64", lambda: synth.c3_layer(32768, 64)
+    yield "c4_sw_layer0", lambda: synth.c4_layer(0)
+    yield "c4_draft_layer48", lambda: synth.c4_layer(48)
+
+
+@pytest.mark.parametrize("name,make", list(_workloads()), ids=[n for n, _ in _workloads()])
+def test_workload_fused_equals_separate(name, make):
+    _fused_vs_separate(make(), name)
+
+
+@pytest.mark.parametrize("split_tiles", [0, 1, 2])
+@pytest.mark.parametrize("block_size", [32, 64])
+def test_ragged_boundaries(block_size, split_tiles):
+    """New positions straddling 32-key tiles, pages and (split_tiles 1, 2) splits; sequences
+    shorter than q_len (positions below 0 are not stored)."""
+    lay = synth.tiny_layer(401 + block_size, [40, 70, 64, 129, 700, 12, 5, 1], num_q_heads=18, num_kv_heads=2,
+                           block_size=block_size, q_len=12, pool_slack=2.0, outlier_rate=0.01)
+    _fused_vs_separate(lay, f"ragged p{block_size} split_tiles {split_tiles}", split_tiles=split_tiles)
+
+
+@pytest.mark.parametrize("row_groups", [1, 2, 4])
+def test_row_groups(row_groups):
+    lay = synth.tiny_layer(409, [3000, 257, 33], num_q_heads=72, num_kv_heads=8, block_size=64, q_len=12)
+    _fused_vs_separate(lay, f"row groups {row_groups}", layout=5, row_groups=row_groups)
+
+
+@pytest.mark.parametrize("window_left", [0, 11, 63, 511])
+def test_sliding_windows(window_left):
+    lay = synth.tiny_layer(411 + window_left, [600, 40, 513], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=12,
+                           window_left=window_left)
+    _fused_vs_separate(lay, f"window {window_left}")
+
+
+def test_single_query():
+    lay = synth.tiny_layer(413, [1, 32, 33, 300], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=1)
+    _fused_vs_separate(lay, "q1")
+
+
+def test_repeated_steps_with_growing_sequences():
+    """Three decode steps in a row on one layer: each fused call inserts at the new tail and
+    attends over everything inserted so far, bitwise equal to insert + decode."""
+    final = synth.tiny_layer(415, [524, 114], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12, pool_slack=2.0)
+    fused, sep = PagedLayer(final), PagedLayer(final)
+    for gl in (fused, sep):
+        for b in range(final.num_seqs):
+            gl.insert_tokens(b, 0, int(final.seq_lens[b]) - 36)
+    for step in range(3):
+        lay = dataclasses.replace(final, seq_lens=(final.seq_lens - 12 * (2 - step)).astype(np.int32))
+        for gl in (fused, sep):
+            gl.lay = lay
+            gl.seq_lens.copy_(torch.from_numpy(lay.seq_lens))
+        fused.stage_new_tokens()
+        out_f = fused.insert_decode().clone()
+        sep.stage_step()
+        sep.insert_step()
+        out_s = sep.decode().clone()
+        torch.cuda.synchronize()
+        assert torch.equal(fused.k_pool, sep.k_pool) and torch.equal(fused.v_pool, sep.v_pool), step
+        assert torch.equal(out_f, out_s), step
+        _check(lay, out_f, f"step {step}")
+
+
+def test_rejects_other_layouts_and_bf16():
+    lay = synth.tiny_layer(417, [100], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
+    gl = PagedLayer(lay, layout=3)
+    gl.prefill()
+    gl.stage_new_tokens()
+    with pytest.raises(fkv.FkvError) as e:
+        gl.insert_decode()
+    assert e.value.status == fkv.EUNSUPPORTED
+    lay16 = synth.tiny_layer(417, [100], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12, cache_dtype="bf16")
+    gl16 = PagedLayer(lay16)
+    gl16.prefill()
+    gl16.stage_new_tokens()
+    with pytest.raises(fkv.FkvError) as e:
+        gl16.insert_decode()
+    assert e.value.status == fkv.EUNSUPPORTED
