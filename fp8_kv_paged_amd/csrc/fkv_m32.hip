@@ -244,7 +244,7 @@ __device__ __forceinline__ void quad_finish(const DecodeArgs& a, int b, int g, i
 
 namespace {
 
-template <int RT, int KL, bool kFp8>
+template <int RT, int KL, bool kFp8, bool kIns>
 __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_m32_kernel(DecodeArgs a) {
   typedef M32Shape<RT, KL, kFp8> S;
   static_assert(kFp8, "the 32-row kernel reads FP8 caches");
@@ -352,7 +352,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   // Fused insert: every group requests the q_len new tokens' K and V of its KV head with Q
   // (thread t < 16 M: K of token t / 16, dims 8 (t % 16) .. +7; the next 16 M threads: V);
   // only the groups whose split holds the new positions use them.
-  const bool fuse_ins = a.k_new != nullptr;
+  constexpr bool fuse_ins = kIns;  // the instantiation with the new tokens' insert (k_new, v_new set)
   const int ci = (int)threadIdx.x < 16 * M ? (int)threadIdx.x : (int)threadIdx.x - 16 * M;  // chunk of K or V
   const bool ins_v_chunk = (int)threadIdx.x >= 16 * M;
   const bool ins_chunk = fuse_ins && (int)threadIdx.x < 32 * M;
@@ -367,9 +367,14 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   // Complete the page-table, Q and new-token loads through an asm that redefines their
   // registers: later reads carry no load dependence, so the compiler adds no wait on the
   // DMAs below, whose counts the loop relies on.
-  asm volatile("s_waitcnt vmcnt(0)"
-               : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]), "+v"(qraw[4]),
-                 "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]), "+v"(nraw), "+v"(vs_ins)::"memory");
+  if constexpr (kIns)
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
+                   "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]), "+v"(nraw), "+v"(vs_ins)::"memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
+                   "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7])::"memory");
   const float C = a.softmax_scale * ks * kLog2e;
   auto block_of = [&](int tile) -> int {
     const int e = (tile >> bshift) - lb0;
@@ -871,8 +876,12 @@ static hipError_t launch_m32_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t per_pair = (int64_t)a.max_splits * a.row_groups;
   const int64_t grid = a.xcd_pairs ? (pairs + 7) / 8 * 8 * per_pair : pairs * per_pair;
-  hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true>), dim3((unsigned)grid), dim3(M32Shape<RT, KL, true>::kThreads),
-                     0, stream, a);
+  if (a.k_new)
+    hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true, true>), dim3((unsigned)grid),
+                       dim3(M32Shape<RT, KL, true>::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true, false>), dim3((unsigned)grid),
+                       dim3(M32Shape<RT, KL, true>::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
