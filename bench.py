@@ -82,7 +82,7 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
         layers.append(c)
     torch.cuda.synchronize()
 
-    fused_ok = cache_dtype == "fp8_e4m3fn" and args.layout in (0, 5)
+    fused_ok = cache_dtype == "fp8_e4m3fn" and args.layout in (0, 5, 6)
     if fused_ok:
         base.stage_new_tokens()
         for c in layers[1:]:
@@ -182,7 +182,7 @@ def cpu_baseline(seconds):
 
 # split kernel each decode layout launches (layout 0, the automatic choice, is the 32-row kernel for FP8)
 DECODE_KERNELS = {0: "decode_m32_kernel", 1: "decode_split_dma_kernel", 2: "decode_split_kernel",
-                  3: "decode_rows_kernel", 4: "decode_wide_kernel", 5: "decode_m32_kernel"}
+                  3: "decode_rows_kernel", 4: "decode_wide_kernel", 5: "decode_m32_kernel", 6: "decode_m32_kernel"}
 
 
 def source_hash():

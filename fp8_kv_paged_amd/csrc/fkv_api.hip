@@ -68,7 +68,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   if (d->num_seqs < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 1)
     return FKV_EINVAL;
   if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
-  if (d->layout < 0 || d->layout > 5) return FKV_EINVAL;
+  if (d->layout < 0 || d->layout > 6) return FKV_EINVAL;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
@@ -81,7 +81,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   if (nt > kMaxNT) return FKV_EUNSUPPORTED;
   if (d->layout == 4 && nt < 3) return FKV_EUNSUPPORTED;  // the wide kernel needs two row halves
   const bool fp8_cache = c->desc.cache_dtype == FKV_FP8_E4M3FN;
-  if (d->layout == 5 && !fp8_cache) return FKV_EUNSUPPORTED;  // the 32-row kernel reads FP8 caches
+  if ((d->layout == 5 || d->layout == 6) && !fp8_cache) return FKV_EUNSUPPORTED;  // the 32-row kernel reads FP8 caches
   p->nt = nt;
   p->rows_pad = 16 * nt;
 
@@ -96,7 +96,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const fkv::SplitShapeInfo sh = fkv::split_shape(nt, d->layout, fp8);
   p->row_groups = 1;
   int64_t tps = d->split_tiles;
-  if (sh.groups_per_cu == -2) {
+  if (sh.groups_per_cu == -2 || sh.groups_per_cu == -3) {
     // 32-row kernel: the rows_pad = 32 * rt_total packed rows of a KV head are cut into RG
     // row groups of separate work groups (on one XCD, sharing K/V tiles through its L2); the
     // splits fill the chip, each key lane takes whole tiles, a split at most 128 tiles.
@@ -112,9 +112,15 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
       // two groups beat one and four at both 8k and 32k context.
       rg = rt_total >= 2 ? 2 : 1;
     }
+    if (sh.groups_per_cu == -3) {
+      // layout 6: two row tiles per work group (both held by each of its four waves)
+      if (rt_total < 2) return FKV_EUNSUPPORTED;
+      if (d->row_groups != 0 && d->row_groups != rt_total / 2) return FKV_EUNSUPPORTED;
+      rg = rt_total / 2;
+    }
     if (rg > rt_total) return FKV_EUNSUPPORTED;
     p->row_groups = rg;
-    const int kl = 8 / (rt_total / rg);
+    const int kl = sh.groups_per_cu == -3 ? 4 : 8 / (rt_total / rg);
     if (tps == 0) {
       const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * rg));
       tps = (tiles_max + splits - 1) / splits;
@@ -155,7 +161,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   p->max_splits = (int)max_splits;
   // Row-group kernel: with at least eight (sequence, KV head) pairs, each pair's work groups
   // go to one XCD (all eight XCDs stay busy); else each split's row groups share one.
-  p->xcd_pairs = ((sh.groups_per_cu == 0 || sh.groups_per_cu == -2) && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
+  p->xcd_pairs = ((sh.groups_per_cu == 0 || sh.groups_per_cu <= -2) && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
   p->fused_combine = 0;
   p->ws_ctl_bytes = 0;
   if (max_splits <= 1) {
@@ -165,7 +171,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const uint64_t parts = (uint64_t)d->num_seqs * hkv * (uint64_t)max_splits;
   p->ws_o_bytes = round_up(parts * p->rows_pad * FKV_HEAD_DIM * sizeof(float), kAlign);
   p->ws_ml_bytes = round_up(parts * 2 * p->rows_pad * sizeof(float), kAlign);
-  if (sh.groups_per_cu == -2) {
+  if (sh.groups_per_cu <= -2) {
     // 32-row kernel: when every work group of the grid fits on the chip at once (one per
     // CU), the splits of a (sequence, KV head) are merged inside the kernel
     const int64_t pairs = (int64_t)d->num_seqs * hkv;
@@ -251,7 +257,7 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   const bool fused_insert = k_new != nullptr;
   const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
   // the fused insert exists in the 32-row kernel only (FP8 cache, layout 5 or automatic)
-  if (fused_insert && (!fp8 || fkv::split_shape(p.nt, p.layout, fp8).groups_per_cu != -2)) return reject(FKV_EUNSUPPORTED);
+  if (fused_insert && (!fp8 || fkv::split_shape(p.nt, p.layout, fp8).groups_per_cu > -2)) return reject(FKV_EUNSUPPORTED);
   if (desc->num_seqs == 0) return FKV_OK;
   if (fused_insert && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return reject(FKV_EINVAL);
   if (!q || !block_table || !seq_lens || !out) return reject(FKV_EINVAL);

@@ -940,8 +940,9 @@ hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool 
   hipError_t e;
   if (shape.groups_per_cu == 0) {
     e = launch_rows(a, shape.ntw, fp8, stream);
-  } else if (shape.groups_per_cu == -2) {
-    e = launch_m32(a, shape.r / a.row_groups, fp8, stream);  // row tiles per work group
+  } else if (shape.groups_per_cu == -2 || shape.groups_per_cu == -3) {
+    // row tiles per work group; layout 6 holds two row tiles per wave
+    e = launch_m32(a, shape.r / a.row_groups, shape.groups_per_cu == -3 ? 2 : 1, fp8, stream);
   } else if (shape.groups_per_cu < 0) {
     e = launch_wide(a, shape.ntw, fp8, stream);
   } else {

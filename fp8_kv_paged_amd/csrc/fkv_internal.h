@@ -79,11 +79,14 @@ struct SplitShapeInfo {
 // row halves, k = 2 key lanes.
 // Layout 5 (FP8 cache): one work group of eight waves per (sequence, KV head, split), the
 // rows cut into r tiles of 32 (1, 2 or 4) and the keys into k = 8 / r lanes
-// (groups_per_cu -2 marks it; ntw = r).
+// (groups_per_cu -2 marks it; ntw = r). Layout 6 (FP8 cache, at least two row tiles): the
+// same plan with two row tiles per work group held by each of its four waves (one per SIMD,
+// k = 4 key lanes); groups_per_cu -3 marks it.
 inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
-  if (layout == 5 || (layout == 0 && fp8)) {  // layout 0 (automatic) is layout 5 for FP8 caches
+  if (layout == 5 || layout == 6 || (layout == 0 && fp8)) {  // layout 0 (automatic) is layout 5 for FP8 caches
     const int rows = 16 * nt;
     const int rt = rows <= 32 ? 1 : (rows <= 64 ? 2 : 4);
+    if (layout == 6) return {rt, rt, 4, -3};
     return {rt, rt, 8 / rt, -2};
   }
   if (layout == 4 && nt >= 3) return {(nt + 1) / 2, 2, 2, -1};
@@ -99,8 +102,9 @@ inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
 
 // Row-group split kernel (layout 3): ntw 16-row tiles per row group.
 hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
-// 32-row tile kernel (layout 5): rt row tiles of 32 (1, 2 or 4), FP8 cache only.
-hipError_t launch_m32(const DecodeArgs& a, int rt, bool fp8, hipStream_t stream);
+// 32-row tile kernel: rt row tiles of 32 per work group (1, 2 or 4) and rw per wave (layout 5:
+// 1; layout 6: 2 with rt = 2), FP8 cache only.
+hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, bool fp8, hipStream_t stream);
 // Wide split kernel (layout 4): ntw 16-row tiles per row half.
 hipError_t launch_wide(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
 // Merges the wide kernel's lane-layout split partials into out.

@@ -48,9 +48,12 @@ namespace {
 
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
-template <int RT, int KL, bool kFp8>
+// RT row tiles of 32 per work group, KL key lanes, RW row tiles per wave: (RT / RW) * KL
+// waves. RW = 1: eight waves, two per SIMD; RW = 2: four waves, one per SIMD, each holding
+// two row tiles so that every converted K/V operand feeds two MFMAs.
+template <int RT, int KL, int RW, bool kFp8>
 struct M32Shape {
-  static constexpr int kWaves = RT * KL;
+  static constexpr int kWaves = RT / RW * KL;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kEs = kFp8 ? 1 : 2;
   static constexpr int kTileBytes = 2 * kTile * kHeadDim * kEs;  // K and V of one 32-key tile
@@ -59,12 +62,14 @@ struct M32Shape {
   static constexpr int kPerWave = KL * kChunks / kWaves;         // DMA instructions per wave per step
   static constexpr int kDepth = (128 * 1024) / kStepBytes < 8 ? (128 * 1024) / kStepBytes : 8;
   static constexpr int kRing = kDepth * kStepBytes;
-  static constexpr int kXch = kWaves * 64 * 64 * 4;              // merge exchange: 64 floats per lane per wave
+  static constexpr int kXch = kWaves * RW * 64 * 64 * 4;         // merge exchange: 64 floats per lane per row tile
   static constexpr int kBody = kRing > kXch ? kRing : kXch;
   static_assert(kDepth >= 2, "ring of at least two steps");
   static_assert((kDepth - 2) * kPerWave <= 63, "vmcnt range");
   static_assert(KL * kChunks % kWaves == 0, "DMA chunks split evenly over the waves");
   static_assert(8 % KL == 0, "output groups split evenly over the key lanes");
+  static_assert(RT % RW == 0 && (RW == 1 || RW == 2), "whole row tiles per wave");
+  static_assert(kWaves == 4 || kWaves == 8, "one or two waves per SIMD");
   static constexpr int kInsLds = 16 * kHeadDim + kHeadDim * 64;  // fused insert: K and V codes
   static_assert(256 + kBody + 2 * KL * RT * 32 * 4 + kInsLds <= 160 * 1024, "LDS budget of one CU");
 };
@@ -73,6 +78,20 @@ struct M32Shape {
 // would split the 256-register budget of a two-wave-per-SIMD kernel in halves.
 __device__ __forceinline__ void pv32_f16(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+// The same product with the accumulator pinned to AGPRs (two row tiles per wave: 128
+// accumulators that would not fit beside the operands in the 256 VGPRs). Only inline asm
+// touches the AGPR copy, so the asm carries the wait states the hazard recognizer cannot
+// see: two after a VALU write of a source VGPR. Back-to-back MFMAs on one accumulator need
+// none.
+__device__ __forceinline__ void pv32_f16_agpr(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Orders every later access of a row tile's AGPR accumulators after the MFMAs in flight on
+// them (a 32x32 MFMA result may be read by other instructions only some passes after the
+// MFMA issues; 24 wait states cover it).
+__device__ __forceinline__ void acc_fence32(f32x16_t (&o)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
 }
 // Maximum of the two lanes that hold one query row (l and l ^ 32).
 __device__ __forceinline__ float pair_max(float x) {
@@ -244,9 +263,9 @@ __device__ __forceinline__ void quad_finish(const DecodeArgs& a, int b, int g, i
 
 namespace {
 
-template <int RT, int KL, bool kFp8, bool kIns>
-__global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_m32_kernel(DecodeArgs a) {
-  typedef M32Shape<RT, KL, kFp8> S;
+template <int RT, int KL, int RW, bool kFp8, bool kIns>
+__global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void decode_m32_kernel(DecodeArgs a) {
+  typedef M32Shape<RT, KL, RW, kFp8> S;
   static_assert(kFp8, "the 32-row kernel reads FP8 caches");
   constexpr int kRows = 32 * RT;
   // (m, l) of every wave's rows, apart from the ring so that its reads never wait for DMAs
@@ -277,7 +296,8 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 
   const int lane = threadIdx.x & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rt = w % RT, kl = w / RT;
+  constexpr int kTG = RT / RW;                // row-tile groups of a work group
+  const int rtg = w % kTG, kl = w / kTG;      // this wave: row tiles rtg * RW .. +RW-1, key lane kl
   const int G = a.group, M = a.q_len, GM = G * M;
   const int wl = a.window_left;
   const int bshift = a.block_size == 64 ? 1 : 0;  // 32-key tiles per page: 1 or 2
@@ -330,51 +350,67 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   const int p_min = L - M;                               // smallest row position
   float ks = *a.k_scale;
 
-  // ---- this wave's query rows and Q operand: lane (n, hh) holds dims 32j + 16hh .. +15
-  const int rl = 32 * rt + n;  // row within the work group (LDS index)
-  const int r = row0 + rl;      // packed row of the KV head
-  const bool row_ok = r < GM;
-  const int rpos = row_ok ? L - M + r / G : -1;
-  const bool wave_rows = row0 + 32 * rt < GM;  // wave-uniform: the row tile holds a real row
-  u32x4_t qraw[8];
-  if (row_ok) {
-    const int i = r / G, hq = g * G + (r - i * G);
-    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim);
+  // ---- this wave's query rows and Q operands: lane (n, hh) of row tile r holds dims
+  // 32j + 16hh .. +15 of row 32 (rtg * RW + r) + n
+  int rl[RW], rpos[RW];
+  u32x4_t qraw[RW][8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      qraw[2 * j] = qp[4 * j + 2 * hh];
-      qraw[2 * j + 1] = qp[4 * j + 2 * hh + 1];
+  for (int r = 0; r < RW; ++r) {
+    rl[r] = 32 * (rtg * RW + r) + n;  // row within the work group (LDS index)
+    const int pr = row0 + rl[r];      // packed row of the KV head
+    rpos[r] = pr < GM ? L - M + pr / G : -1;
+    if (pr < GM) {
+      const int i = pr / G, hq = g * G + (pr - i * G);
+      const u32x4_t* qp =
+          reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qraw[r][2 * j] = qp[4 * j + 2 * hh];
+        qraw[r][2 * j + 1] = qp[4 * j + 2 * hh + 1];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qraw[r][c] = u32x4_t{0u, 0u, 0u, 0u};
     }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qraw[c] = u32x4_t{0u, 0u, 0u, 0u};
   }
+  const bool wave_rows = row0 + 32 * rtg * RW < GM;  // wave-uniform: the wave's row tiles hold a real row
   // Fused insert: every group requests the q_len new tokens' K and V of its KV head with Q
   // (thread t < 16 M: K of token t / 16, dims 8 (t % 16) .. +7; the next 16 M threads: V);
   // only the groups whose split holds the new positions use them.
   constexpr bool fuse_ins = kIns;  // the instantiation with the new tokens' insert (k_new, v_new set)
-  const int ci = (int)threadIdx.x < 16 * M ? (int)threadIdx.x : (int)threadIdx.x - 16 * M;  // chunk of K or V
-  const bool ins_v_chunk = (int)threadIdx.x >= 16 * M;
-  const bool ins_chunk = fuse_ins && (int)threadIdx.x < 32 * M;
-  u32x4_t nraw{0u, 0u, 0u, 0u};
+  constexpr int kInsPer = 512 / S::kThreads;  // chunks per thread (32 M <= 512)
+  int ci[kInsPer];
+  bool ins_v_chunk[kInsPer], ins_chunk[kInsPer];
+  u32x4_t nraw[kInsPer];
   float vs_ins = 1.0f;
-  if (ins_chunk) {
-    const uint16_t* src = (ins_v_chunk ? a.v_new : a.k_new) +
-                          (((int64_t)b * M + (ci >> 4)) * a.num_kv_heads + g) * kHeadDim + 8 * (ci & 15);
-    nraw = *reinterpret_cast<const u32x4_t*>(src);
-    vs_ins = *a.v_scale;
+#pragma unroll
+  for (int u = 0; u < kInsPer; ++u) {
+    const int t = (int)threadIdx.x + u * S::kThreads;
+    ci[u] = t < 16 * M ? t : t - 16 * M;  // chunk of K or V
+    ins_v_chunk[u] = t >= 16 * M;
+    ins_chunk[u] = fuse_ins && t < 32 * M;
+    nraw[u] = u32x4_t{0u, 0u, 0u, 0u};
+    if (ins_chunk[u]) {
+      const uint16_t* src = (ins_v_chunk[u] ? a.v_new : a.k_new) +
+                            (((int64_t)b * M + (ci[u] >> 4)) * a.num_kv_heads + g) * kHeadDim + 8 * (ci[u] & 15);
+      nraw[u] = *reinterpret_cast<const u32x4_t*>(src);
+      vs_ins = *a.v_scale;
+    }
   }
   // Complete the page-table, Q and new-token loads through an asm that redefines their
   // registers: later reads carry no load dependence, so the compiler adds no wait on the
   // DMAs below, whose counts the loop relies on.
-  if constexpr (kIns)
-    asm volatile("s_waitcnt vmcnt(0)"
-                 : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
-                   "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7]), "+v"(nraw), "+v"(vs_ins)::"memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)"
-                 : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks), "+v"(qraw[0]), "+v"(qraw[1]), "+v"(qraw[2]), "+v"(qraw[3]),
-                   "+v"(qraw[4]), "+v"(qraw[5]), "+v"(qraw[6]), "+v"(qraw[7])::"memory");
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(bt_lo), "+v"(bt_hi), "+v"(ks)::"memory");
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+    asm volatile(""
+                 : "+v"(qraw[r][0]), "+v"(qraw[r][1]), "+v"(qraw[r][2]), "+v"(qraw[r][3]), "+v"(qraw[r][4]),
+                   "+v"(qraw[r][5]), "+v"(qraw[r][6]), "+v"(qraw[r][7])::"memory");
+  if constexpr (kIns) {
+#pragma unroll
+    for (int u = 0; u < kInsPer; ++u) asm volatile("" : "+v"(nraw[u])::"memory");
+    asm volatile("" : "+v"(vs_ins)::"memory");
+  }
   const float C = a.softmax_scale * ks * kLog2e;
   auto block_of = [&](int tile) -> int {
     const int e = (tile >> bshift) - lb0;
@@ -418,39 +454,53 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   };
   const uint32_t ring_lane = (uint32_t)(uintptr_t)body + (uint32_t)(kl * S::kTileBytes) + 16u * (uint32_t)lane;
 
-  // ---- online-softmax state of the lane's row
-  f32x16_t o[4];
+  // ---- online-softmax state of the lane's rows (one per row tile of the wave)
+  f32x16_t o[RW][4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
-  float m_ref = kRefInit, lsum = 0.f;
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[r][dt][v] = 0.f;
+  float m_ref[RW], lsum[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    m_ref[r] = kRefInit;
+    lsum[r] = 0.f;
+  }
 
-  // ---- S^T = K Q^T of one tile (fp8 -> bf16 conversions feed the MFMAs one chunk at a time)
-  auto qk = [&](const TileRegs32<true>& x, f32x16_t& sc) {
+  // ---- S^T = K Q^T of one tile for every row tile of the wave (each fp8 -> bf16 K chunk
+  // is converted once and feeds one MFMA per row tile)
+  auto qk = [&](const TileRegs32<true>& x, f32x16_t (&sc)[RW]) {
     const u32x4_t kraw[4] = {x.k[0][0], x.k[0][1], x.k[1][0], x.k[1][1]};
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sc[v] = 0.f;
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sc[r][v] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const u32x4_t& kr = kraw[c >> 1];
       const bf16x8_t kf = fp8x8_to_bf16x8(kr[(c & 1) * 2], kr[(c & 1) * 2 + 1]);
-      sc = mfma32_bf16(kf, __builtin_bit_cast(bf16x8_t, qraw[c]), sc);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) sc[r] = mfma32_bf16(kf, __builtin_bit_cast(bf16x8_t, qraw[r][c]), sc[r]);
     }
   };
   // ---- masking of a tile that is not visible to every row of the KV head: invisible
   // scores become -inf; keys outside [lo_u, L), and every key of an invalid block, may hold
   // stale bytes, so their V bytes are zeroed (0 * NaN cannot occur)
-  auto mask = [&](int tile, f32x16_t& sc, TileRegs32<true>& x) {
+  auto mask = [&](int tile, f32x16_t (&sc)[RW], TileRegs32<true>& x) {
     const int kt = tile * kTile;
     const bool valid = (unsigned)block_of(tile) < (unsigned)a.num_blocks;
-    const int hi = valid ? rpos : -1;
-    const int lo = (wl < 0) ? 0 : max(0, rpos - wl);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = kt + 16 * (v >> 3) + 8 * hh + (v & 7);
-      const uint32_t bad = (uint32_t)(((j - lo) | (hi - j)) >> 31);
-      sc[v] = __uint_as_float((bad & 0xFF800000u) | (~bad & __float_as_uint(sc[v])));
+    for (int r = 0; r < RW; ++r) {
+      const int hi = valid ? rpos[r] : -1;
+      const int lo = (wl < 0) ? 0 : max(0, rpos[r] - wl);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int j = kt + 16 * (v >> 3) + 8 * hh + (v & 7);
+        const uint32_t bad = (uint32_t)(((j - lo) | (hi - j)) >> 31);
+        sc[r][v] = __uint_as_float((bad & 0xFF800000u) | (~bad & __float_as_uint(sc[r][v])));
+      }
     }
 #pragma unroll
     for (int cp = 0; cp < 2; ++cp) {
@@ -475,11 +525,12 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
     const int kt = tile * kTile;
     return ((unsigned)block_of(tile) < (unsigned)a.num_blocks) && (kt >= lo_max) && (kt + kTile - 1 <= p_min);
   };
-  // ---- probabilities against the current reference; the lane's sum is the range check
-  auto probs = [&](const f32x16_t& sc, uint32_t (&hw)[8]) -> float {
+  // ---- probabilities of row tile r against its current reference; the lane's sum is the
+  // range check
+  auto probs = [&](const f32x16_t& sc, float mr, uint32_t (&hw)[8]) -> float {
     float p[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(sc[v], C, -m_ref));
+    for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(sc[v], C, -mr));
 #pragma unroll
     for (int k = 0; k < 8; ++k) hw[k] = pack_f16(p[2 * k], p[2 * k + 1]);
     // the row sum uses the same rounded probabilities the PV product sees
@@ -491,33 +542,49 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   };
   // cold path: exact row maximum; raise the reference of rows exceeded by more than
   // kLazyTau, rescale those rows, recompute the probabilities
-  auto raise = [&](const f32x16_t& sc, uint32_t (&hw)[8], float& lt) {
+  auto raise = [&](int r, const f32x16_t& sc, uint32_t (&hw)[8], float& lt) {
     float mx = sc[0];
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
     const float cand = pair_max(mx) * C;  // -inf when the row sees no key of this tile
-    const bool up = cand > m_ref + kLazyTau;
+    const bool up = cand > m_ref[r] + kLazyTau;
     if (__builtin_amdgcn_ballot_w64(up) != 0) {
-      const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - cand) : 1.0f;
-      lsum *= alpha;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m_ref[r] - cand) : 1.0f;
+      lsum[r] *= alpha;
+      if constexpr (RW == 2) acc_fence32(o[r]);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      m_ref = up ? cand : m_ref;
-      lt = probs(sc, hw);
+      for (int dt = 0; dt < 4; ++dt) o[r][dt] *= alpha;
+      m_ref[r] = up ? cand : m_ref[r];
+      lt = probs(sc, m_ref[r], hw);
     }
   };
-  // ---- O^T += V^T P^T: d-tile 2a+b, key half c' reads bytes 8b..8b+7 of V chunk (c', a)
-  auto pv = [&](const TileRegs32<true>& x, const uint32_t (&hw)[8]) {
-    const f16x8_t P0 = __builtin_bit_cast(f16x8_t, u32x4_t{hw[0], hw[1], hw[2], hw[3]});
-    const f16x8_t P1 = __builtin_bit_cast(f16x8_t, u32x4_t{hw[4], hw[5], hw[6], hw[7]});
+  // ---- O^T += V^T P^T: d-tile 2a+b, key half c' reads bytes 8b..8b+7 of V chunk (c', a);
+  // each converted V operand feeds one MFMA per row tile
+  auto pv = [&](const TileRegs32<true>& x, const uint32_t (&hw)[RW][8]) {
+    f16x8_t P0[RW], P1[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      P0[r] = __builtin_bit_cast(f16x8_t, u32x4_t{hw[r][0], hw[r][1], hw[r][2], hw[r][3]});
+      P1[r] = __builtin_bit_cast(f16x8_t, u32x4_t{hw[r][4], hw[r][5], hw[r][6], hw[r][7]});
+    }
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const u32x4_t& v0 = x.v[aa];
         const u32x4_t& v1 = x.v[2 + aa];
-        pv32_f16(o[2 * aa + bb], fp8x8_to_f16x8(v0[2 * bb], v0[2 * bb + 1]), P0);
-        pv32_f16(o[2 * aa + bb], fp8x8_to_f16x8(v1[2 * bb], v1[2 * bb + 1]), P1);
+        const f16x8_t va = fp8x8_to_f16x8(v0[2 * bb], v0[2 * bb + 1]);
+        const f16x8_t vb = fp8x8_to_f16x8(v1[2 * bb], v1[2 * bb + 1]);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          if constexpr (RW == 2) {
+            pv32_f16_agpr(o[r][2 * aa + bb], va, P0[r]);
+            pv32_f16_agpr(o[r][2 * aa + bb], vb, P1[r]);
+          } else {
+            pv32_f16(o[r][2 * aa + bb], va, P0[r]);
+            pv32_f16(o[r][2 * aa + bb], vb, P1[r]);
+          }
+        }
       }
   };
 
@@ -534,32 +601,36 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   const int tn0 = pn0 / kTile;    // first tile holding a new key
   const bool ins = fuse_ins && L > pn0 && pn0 < te * kTile && L > tb * kTile;  // uniform
   if (ins) {
-    const int p = L - M + (ci >> 4);  // this thread's token position
-    // physical block of p from the split's page-table window (lanes hold entries lb0 + lane
-    // and lb0 + 64 + lane); positions outside the split are not stored
-    const int e = min(max((p >> (5 + bshift)) - lb0, 0), 127);
-    const int blo = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_lo);
-    const int bhi = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_hi);
-    const int blk = e < 64 ? blo : bhi;
-    if (ins_chunk && p >= 0) {
-      uint32_t c0, c1;
-      e4m3_encode8(nraw, ins_v_chunk ? vs_ins : ks, c0, c1);
-      const int d0 = 8 * (ci & 15);
-      if (!ins_v_chunk) {
-        *reinterpret_cast<u32x2_t*>(ins_k + (ci >> 4) * kHeadDim + d0) = u32x2_t{c0, c1};
-      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ins_v[(d0 + j) * 64 + (p - kTile * tn0)] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
-      }
-      if (rg == 0 && p >= tb * kTile && p < te * kTile && (unsigned)blk < (unsigned)a.num_blocks) {
-        const int off = p & (a.block_size - 1);
-        const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes;
-        if (!ins_v_chunk) {
-          *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) = u32x2_t{c0, c1};
+    for (int u = 0; u < kInsPer; ++u) {
+      const int p = L - M + (ci[u] >> 4);  // this chunk's token position
+      // physical block of p from the split's page-table window (lanes hold entries lb0 +
+      // lane and lb0 + 64 + lane); positions outside the split are not stored
+      const int e = min(max((p >> (5 + bshift)) - lb0, 0), 127);
+      const int blo = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_lo);
+      const int bhi = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_hi);
+      const int blk = e < 64 ? blo : bhi;
+      if (ins_chunk[u] && p >= 0) {
+        uint32_t c0, c1;
+        e4m3_encode8(nraw[u], ins_v_chunk[u] ? vs_ins : ks, c0, c1);
+        const int d0 = 8 * (ci[u] & 15);
+        if (!ins_v_chunk[u]) {
+          *reinterpret_cast<u32x2_t*>(ins_k + (ci[u] >> 4) * kHeadDim + d0) = u32x2_t{c0, c1};
         } else {
-          uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + slab + (off >> 3) * 1024 + d0 * 8 + (off & 7);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) vp[j * 8] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
+          for (int j = 0; j < 8; ++j)
+            ins_v[(d0 + j) * 64 + (p - kTile * tn0)] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
+        }
+        if (rg == 0 && p >= tb * kTile && p < te * kTile && (unsigned)blk < (unsigned)a.num_blocks) {
+          const int off = p & (a.block_size - 1);
+          const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes;
+          if (!ins_v_chunk[u]) {
+            *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) = u32x2_t{c0, c1};
+          } else {
+            uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + slab + (off >> 3) * 1024 + d0 * 8 + (off & 7);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vp[j * 8] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
+          }
         }
       }
     }
@@ -615,7 +686,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   asm volatile("s_barrier" ::: "memory");
   if (S::kDepth - 1 < nsteps) issue(S::kDepth - 1);
   TileRegs32<true> xa, xb;
-  f32x16_t sa, sb;
+  f32x16_t sa[RW], sb[RW];
   if (nfull > 0) {
     read_slot<true>(slot0, xa);
     if (has_new(tb + kl)) patch(tb + kl, xa);
@@ -630,58 +701,78 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
     if (i >= nfull) continue;  // wave-uniform: no tile of this wave at step i (barriers still counted)
     const int tile = tb + KL * i + kl;
     if (!interior(tile)) mask(tile, sa, xa);
-    uint32_t hw[8];
-    float lt;
+    uint32_t hw[RW][8];
+    float lt[RW];
     if (i + 1 < nfull) {
       read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xb);
       if (has_new(tile + KL)) patch(tile + KL, xb);
       // S^T of the next tile interleaved with this tile's probabilities
       qk(xb, sb);
-      lt = probs(sa, hw);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
     } else {
-      lt = probs(sa, hw);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
     }
-    if (__builtin_amdgcn_ballot_w64(!(lt <= kAcceptSum)) != 0) raise(sa, hw, lt);
-    lsum += lt;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      if (__builtin_amdgcn_ballot_w64(!(lt[r] <= kAcceptSum)) != 0) raise(r, sa[r], hw[r], lt[r]);
+      lsum[r] += lt[r];
+    }
     pv(xa, hw);
     xa = xb;
-    sa = sb;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) sa[r] = sb[r];
   }
 
   // ---- merge the KL key lanes of each row tile in a fixed order
-  const float lrow = pair_sum(lsum);
-  if (hh == 0) {
-    sm_m[kl * kRows + rl] = m_ref;
-    sm_l[kl * kRows + rl] = lrow;
+  if constexpr (RW == 2) {
+    acc_fence32(o[0]);
+    acc_fence32(o[1]);
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const float lrow = pair_sum(lsum[r]);
+    if (hh == 0) {
+      sm_m[kl * kRows + rl[r]] = m_ref[r];
+      sm_l[kl * kRows + rl[r]] = lrow;
+    }
   }
   __syncthreads();  // also: every ring read is done, the ring area is free
-  float Mrow = sm_m[rl];
+  float Mrow[RW], Lrow[RW], asf[RW];
 #pragma unroll
-  for (int k = 1; k < KL; ++k) Mrow = fmaxf(Mrow, sm_m[k * kRows + rl]);
-  float Lrow = 0.f;
+  for (int r = 0; r < RW; ++r) {
+    Mrow[r] = sm_m[rl[r]];
 #pragma unroll
-  for (int k = 0; k < KL; ++k) Lrow += sm_l[k * kRows + rl] * __builtin_amdgcn_exp2f(sm_m[k * kRows + rl] - Mrow);
-  const float asf = __builtin_amdgcn_exp2f(m_ref - Mrow);
+    for (int k = 1; k < KL; ++k) Mrow[r] = fmaxf(Mrow[r], sm_m[k * kRows + rl[r]]);
+    Lrow[r] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KL; ++k)
+      Lrow[r] += sm_l[k * kRows + rl[r]] * __builtin_amdgcn_exp2f(sm_m[k * kRows + rl[r]] - Mrow[r]);
+    asf[r] = __builtin_amdgcn_exp2f(m_ref[r] - Mrow[r]);
+  }
   // Output group gi = 4a + i holds dims 64a + 16i + 8hh + 0..7: elements 4i..4i+3 of d-tiles
   // 2a and 2a + 1. Key lane kl owns groups kl*GPK .. +GPK-1 and receives them from the others.
   constexpr int kGpk = 8 / KL;
-  // [owner][rt][source][kGpk*2 quads][64 lanes][4 floats]: 16-byte, lane-contiguous accesses
+  // [owner][row tile][source][kGpk*2 quads][64 lanes][4 floats]: 16-byte, lane-contiguous accesses
   f32x4_t* xch = reinterpret_cast<f32x4_t*>(body);
-  auto xidx = [&](int owner, int src, int f4) -> int {
+  auto xidx = [&](int owner, int rt, int src, int f4) -> int {
     return (((owner * RT + rt) * KL + src) * (kGpk * 2) + f4) * 64 + lane;
   };
 #pragma unroll
-  for (int gi = 0; gi < 8; ++gi) {
-    const int owner = gi / kGpk;
-    if (owner == kl) continue;
-    const int aa = gi >> 2, ii = gi & 3;
+  for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const f32x16_t& acc = o[2 * aa + bb];
-      xch[xidx(owner, kl, (gi % kGpk) * 2 + bb)] =
-          f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf;
+    for (int gi = 0; gi < 8; ++gi) {
+      const int owner = gi / kGpk;
+      if (owner == kl) continue;
+      const int aa = gi >> 2, ii = gi & 3;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const f32x16_t& acc = o[r][2 * aa + bb];
+        xch[xidx(owner, rtg * RW + r, kl, (gi % kGpk) * 2 + bb)] =
+            f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf[r];
+      }
     }
-  }
   __syncthreads();
   const bool direct = (nsplit == 1);
   const float vsc = *a.v_scale;
@@ -690,41 +781,47 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
   // staged row-major in LDS (rows padded to kStageStride floats: conflict-free) so that the
   // group's stores write whole contiguous rows.
   constexpr int kStageStride = kHeadDim + 4;
-  float o8s[kGpk][8];
+  float o8s[RW][kGpk][8];
 #pragma unroll
-  for (int gi = 0; gi < 8; ++gi) {
-    // compile-time group index (the accumulators are only indexed by constants)
-    if (gi / kGpk != kl) continue;
-    const int gl = gi % kGpk;
-    const int aa = gi >> 2, ii = gi & 3;
+  for (int r = 0; r < RW; ++r)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o8s[gl][e] = 0.f;
+    for (int gi = 0; gi < 8; ++gi) {
+      // compile-time group index (the accumulators are only indexed by constants)
+      if (gi / kGpk != kl) continue;
+      const int gl = gi % kGpk;
+      const int aa = gi >> 2, ii = gi & 3;
 #pragma unroll
-    for (int src = 0; src < KL; ++src) {
+      for (int e = 0; e < 8; ++e) o8s[r][gl][e] = 0.f;
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        const f32x16_t& acc = o[2 * aa + bb];
-        const f32x4_t val = (src == kl) ? f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf
-                                        : xch[xidx(kl, src, gl * 2 + bb)];
+      for (int src = 0; src < KL; ++src) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o8s[gl][2 * k + bb] += val[k];
+        for (int bb = 0; bb < 2; ++bb) {
+          const f32x16_t& acc = o[r][2 * aa + bb];
+          const f32x4_t val = (src == kl)
+                                  ? f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf[r]
+                                  : xch[xidx(kl, rtg * RW + r, src, gl * 2 + bb)];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o8s[r][gl][2 * k + bb] += val[k];
+        }
       }
     }
-  }
   float* stage = reinterpret_cast<float*>(body);  // [kRows][kStageStride], over the exchange area
   float* sm_row = sm_ml;                          // merged (M, L) per row, over the per-lane (m, l)
   __syncthreads();  // every exchange and (m, l) read is done
 #pragma unroll
-  for (int gl = 0; gl < kGpk; ++gl) {
-    const int gi = kl * kGpk + gl;
-    const int d0 = 64 * (gi >> 2) + 16 * (gi & 3) + 8 * hh;
-    float* st = stage + rl * kStageStride + d0;
-    *reinterpret_cast<f32x4_t*>(st) = f32x4_t{o8s[gl][0], o8s[gl][1], o8s[gl][2], o8s[gl][3]};
-    *reinterpret_cast<f32x4_t*>(st + 4) = f32x4_t{o8s[gl][4], o8s[gl][5], o8s[gl][6], o8s[gl][7]};
-  }
-  if (kl == 0 && hh == 0) {
-    sm_row[rl] = Mrow;
-    sm_row[kRows + rl] = Lrow;
+  for (int r = 0; r < RW; ++r) {
+#pragma unroll
+    for (int gl = 0; gl < kGpk; ++gl) {
+      const int gi = kl * kGpk + gl;
+      const int d0 = 64 * (gi >> 2) + 16 * (gi & 3) + 8 * hh;
+      float* st = stage + rl[r] * kStageStride + d0;
+      *reinterpret_cast<f32x4_t*>(st) = f32x4_t{o8s[r][gl][0], o8s[r][gl][1], o8s[r][gl][2], o8s[r][gl][3]};
+      *reinterpret_cast<f32x4_t*>(st + 4) = f32x4_t{o8s[r][gl][4], o8s[r][gl][5], o8s[r][gl][6], o8s[r][gl][7]};
+    }
+    if (kl == 0 && hh == 0) {
+      sm_row[rl[r]] = Mrow[r];
+      sm_row[kRows + rl[r]] = Lrow[r];
+    }
   }
   __syncthreads();
   const int nrows = max(0, min(kRows, GM - row0));  // real rows of this work group
@@ -871,26 +968,26 @@ __global__ __launch_bounds__((M32Shape<RT, KL, kFp8>::kThreads), 1) void decode_
 
 }  // namespace
 
-template <int RT, int KL>
+template <int RT, int KL, int RW>
 static hipError_t launch_m32_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
   const int64_t per_pair = (int64_t)a.max_splits * a.row_groups;
   const int64_t grid = a.xcd_pairs ? (pairs + 7) / 8 * 8 * per_pair : pairs * per_pair;
+  constexpr int kThreads = M32Shape<RT, KL, RW, true>::kThreads;
   if (a.k_new)
-    hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true, true>), dim3((unsigned)grid),
-                       dim3(M32Shape<RT, KL, true>::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_m32_kernel<RT, KL, RW, true, true>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_m32_kernel<RT, KL, true, false>), dim3((unsigned)grid),
-                       dim3(M32Shape<RT, KL, true>::kThreads), 0, stream, a);
+    hipLaunchKernelGGL((decode_m32_kernel<RT, KL, RW, true, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_m32(const DecodeArgs& a, int rt, bool fp8, hipStream_t stream) {
+hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, bool fp8, hipStream_t stream) {
   if (!fp8) return hipErrorInvalidValue;
+  if (rw == 2) return rt == 2 ? launch_m32_t<2, 4, 2>(a, stream) : hipErrorInvalidValue;
   switch (rt) {
-    case 1: return launch_m32_t<1, 8>(a, stream);
-    case 2: return launch_m32_t<2, 4>(a, stream);
-    case 4: return launch_m32_t<4, 2>(a, stream);
+    case 1: return launch_m32_t<1, 8, 1>(a, stream);
+    case 2: return launch_m32_t<2, 4, 1>(a, stream);
+    case 4: return launch_m32_t<4, 2, 1>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

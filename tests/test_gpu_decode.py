@@ -32,10 +32,12 @@ def _check(lay, out, seqs=None, kv_heads=None, tol=parity.ATTN_TOL, label=""):
 
 def _layer(lay, **kw):
     """Built PagedLayer, or None after checking that the layout rejects the shape (layout 4
-    keeps two halves of the query rows, so it needs at least three row tiles; layout 5
-    reads FP8 caches only)."""
+    keeps two halves of the query rows, so it needs at least three row tiles; layouts 5 and
+    6 read FP8 caches only, and layout 6 needs at least two 32-row tiles)."""
     nt = (lay.num_q_heads // lay.num_kv_heads * lay.q_len + 15) // 16
-    if (kw.get("layout") == 4 and nt < 3) or (kw.get("layout") == 5 and lay.cache_dtype != "fp8_e4m3fn"):
+    fp8 = lay.cache_dtype == "fp8_e4m3fn"
+    if ((kw.get("layout") == 4 and nt < 3) or (kw.get("layout") == 5 and not fp8)
+            or (kw.get("layout") == 6 and (not fp8 or nt < 3))):
         with pytest.raises(fkv.FkvError) as e:
             PagedLayer(lay, **kw)
         assert e.value.status == fkv.EUNSUPPORTED
@@ -55,7 +57,7 @@ def _workloads():
     yield "c4_draft_layer48", lambda: synth.c4_layer(48)
 
 
-@pytest.mark.parametrize("layout", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("layout", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("name,make", list(_workloads()), ids=[n for n, _ in _workloads()])
 def test_workload_parity(name, make, layout):
     lay = make()
@@ -139,7 +141,7 @@ def test_edge_cases(case, layout):
     _check(lay, out, label=f"{case} layout {layout}")
 
 
-@pytest.mark.parametrize("layout", [1, 3, 4, 5])
+@pytest.mark.parametrize("layout", [1, 3, 4, 5, 6])
 @pytest.mark.parametrize("split_tiles", [1, 2, 3, 8, 128])
 def test_split_granularity(split_tiles, layout):
     lay = synth.tiny_layer(77, [2000, 64, 900], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12)
@@ -225,3 +227,25 @@ def test_row_groups_parity(name, make, row_groups):
     out = gl.decode()
     torch.cuda.synchronize()
     _check(lay, out, label=f"{name} layout 5 row groups {row_groups}")
+
+
+@pytest.mark.parametrize("name,make,q_len", [
+    ("c2", synth.c2_layer, 12), ("c3_8k_p64", lambda: synth.c3_layer(8192, 64), 12),
+    ("c4_sw_layer0", lambda: synth.c4_layer(0), 12),
+    ("ragged_m6", lambda: synth.tiny_layer(121, [3000, 40, 700], num_q_heads=18, num_kv_heads=2, block_size=32,
+                                            q_len=6, outlier_rate=0.01), 6),
+    ("ragged_m12_p64", lambda: synth.tiny_layer(123, [5000, 13, 12, 257], num_q_heads=72, num_kv_heads=8,
+                                                block_size=64, q_len=12), 12)],
+    ids=["c2", "c3_8k_p64", "c4_sw", "ragged_m6", "ragged_m12_p64"])
+@pytest.mark.parametrize("split_tiles", [0, 4])
+def test_two_row_tiles_per_wave_is_bitwise_layout5(name, make, q_len, split_tiles):
+    """Layout 6 (four waves, each holding two row tiles) does per row tile exactly the
+    arithmetic of layout 5 with two row tiles per work group: outputs are bitwise equal."""
+    lay = make()
+    rows = lay.num_q_heads // lay.num_kv_heads * q_len
+    rt_total = 1 if rows <= 32 else (2 if rows <= 64 else 4)
+    out6 = PagedLayer(lay, layout=6, split_tiles=split_tiles).build().decode().clone()
+    out5 = PagedLayer(lay, layout=5, row_groups=rt_total // 2, split_tiles=split_tiles).build().decode().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out5, out6), name
+    _check(lay, out6, label=f"{name} layout 6 split_tiles {split_tiles}")

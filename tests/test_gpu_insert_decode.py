@@ -91,10 +91,16 @@ def test_ragged_boundaries(block_size, split_tiles):
     _fused_vs_separate(lay, f"ragged p{block_size} split_tiles {split_tiles}", split_tiles=split_tiles)
 
 
-@pytest.mark.parametrize("row_groups", [1, 2, 4])
-def test_row_groups(row_groups):
+@pytest.mark.parametrize("layout,row_groups", [(5, 1), (5, 2), (5, 4), (6, 0)])
+def test_row_groups(layout, row_groups):
     lay = synth.tiny_layer(409, [3000, 257, 33], num_q_heads=72, num_kv_heads=8, block_size=64, q_len=12)
-    _fused_vs_separate(lay, f"row groups {row_groups}", layout=5, row_groups=row_groups)
+    _fused_vs_separate(lay, f"layout {layout} row groups {row_groups}", layout=layout, row_groups=row_groups)
+
+
+@pytest.mark.parametrize("name,make", [("c3_8k_p64", lambda: synth.c3_layer(8192, 64)), ("c2", synth.c2_layer)],
+                         ids=["c3_8k_p64", "c2"])
+def test_layout6_fused(name, make):
+    _fused_vs_separate(make(), f"{name} layout 6", layout=6)
 
 
 @pytest.mark.parametrize("window_left", [0, 11, 63, 511])
