@@ -256,7 +256,7 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   if (rc) return reject(rc);
   const bool fused_insert = k_new != nullptr;
   const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
-  // the fused insert exists in the 32-row kernel only (FP8 cache, layout 5 or automatic)
+  // the fused insert exists in the 32-row kernel only (FP8 cache, layout 5, 6 or automatic)
   if (fused_insert && (!fp8 || fkv::split_shape(p.nt, p.layout, fp8).groups_per_cu > -2)) return reject(FKV_EUNSUPPORTED);
   if (desc->num_seqs == 0) return FKV_OK;
   if (fused_insert && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return reject(FKV_EINVAL);

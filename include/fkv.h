@@ -138,7 +138,7 @@ typedef struct fkv_decode_desc {
   float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
   int32_t out_dtype;           /* FKV_OUT_F32                                               */
   int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
-                                  (at most 128 with layouts 0, 1, 3, 4 and 5)               */
+                                  (at most 128 with layouts 0, 1, 3, 4, 5 and 6)            */
   int32_t layout;              /* work-group layout: 0 = automatic (layout 5 for an FP8 cache,
                                   layout 3 for a BF16 cache); 1 = query rows spread over
                                   row groups of at most 32 rows per wave (two waves per SIMD);
@@ -152,10 +152,16 @@ typedef struct fkv_decode_desc {
                                   5 = 32-row tiles (MFMA 32x32x16), eight waves per work
                                   group, the split's rows in row_groups work groups on one
                                   XCD; splits merged inside the kernel when the grid fits on
-                                  the chip (FP8 cache only, else FKV_EUNSUPPORTED)          */
+                                  the chip (FP8 cache only, else FKV_EUNSUPPORTED);
+                                  6 = layout 5 with two row tiles per work group, both held
+                                  by each of its four waves (one per SIMD); results bitwise
+                                  equal to layout 5 with the same row tiles per work group
+                                  (FP8 cache and at least 33 packed rows, else
+                                  FKV_EUNSUPPORTED)                                         */
   int32_t row_groups;          /* layout 5: work groups sharing one split's query rows (1, 2
                                   or 4, at most the number of 32-row tiles; 0 = automatic);
-                                  ignored by the other layouts                              */
+                                  layout 6: 0 or the number of 32-row tiles / 2 (else
+                                  FKV_EUNSUPPORTED); ignored by the other layouts           */
 } fkv_decode_desc;
 
 /*
@@ -219,7 +225,7 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
  * The pool bytes written are those fkv_insert writes for the same tokens, and out is
  * bitwise equal to fkv_decode_attn's after that insert. The attention reads the new
  * keys from the codes it computed, not back from the pool, so no ordering between
- * the two is needed. FP8 cache and layout 0 or 5 only (else FKV_EUNSUPPORTED).
+ * the two is needed. FP8 cache and layout 0, 5 or 6 only (else FKV_EUNSUPPORTED).
  * Errors: as fkv_decode_attn, plus FKV_EINVAL for a null or misaligned k_new/v_new.
  */
 int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
