@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--ab", action="store_true", help="also time the page-size A/B and 32k context")
+    p.add_argument("--suite", action="store_true",
+                   help="also time the other workloads (C1, C2, the C4 cycle eager and as a HIP graph, C5)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device-to-device copies of MIB MiB (scales the HBM byte counters)")
     return p.parse_args()
@@ -145,6 +147,134 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
     res.update(step_ms=mean(step_ms), insert_ms=mean(ins_ms), decode_ms=mean(dec_ms), decode_ms_median=med(dec_ms),
                combine=cnt["decode_combine_launches"] > 0, fused=cnt["decode_combine_launches"] == 0)
     return res
+
+
+def _time_calls(fn, stream, iters, warmup):
+    """Median and mean event time (ms) of fn() on stream."""
+    import torch
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+        stream.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        stream.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return t[len(t) // 2], sum(t) / len(t)
+
+
+def _visible_kv_bytes(lay, elem):
+    """Algorithmic K/V bytes of one decode call: every key visible to some row, once."""
+    tot = 0
+    for L in lay.seq_lens:
+        L = int(L)
+        lo = 0 if lay.window_left < 0 else max(0, L - lay.q_len - lay.window_left)
+        tot += (L - lo) * lay.num_kv_heads * 2 * 128 * elem
+    return tot
+
+
+def run_suite(iters):
+    """The other workloads of the scope table, timed with HIP events (median):
+    C1 / C2 single layers, the 54-layer C4 cycle eager and as a captured HIP graph, and the
+    32-sequence C5 batch with FP8 and BF16 caches at M = 1 and 12."""
+    import torch
+    from fp8_kv_paged_amd import synth
+    from fp8_kv_paged_amd.layer import PagedLayer
+    stream = torch.cuda.Stream()
+    out = {}
+
+    def layer_step(lay, fused=True):
+        gl = PagedLayer(lay)
+        gl.prefill()
+        gl.stage_step()
+        if fused:
+            gl.stage_new_tokens()
+        return gl
+
+    for name, make in (("c1", synth.c1_layer), ("c2", synth.c2_layer)):
+        lay = make()
+        gl = layer_step(lay)
+        fm, _ = _time_calls(lambda: gl.insert_decode(stream), stream, iters, 20)
+        dm, _ = _time_calls(lambda: gl.decode(stream), stream, iters, 20)
+        im, _ = _time_calls(lambda: gl.insert_step(stream), stream, iters, 20)
+        kv = _visible_kv_bytes(lay, 1)
+        out[name] = {"fused_step_us": round(fm * 1e3, 3), "decode_us": round(dm * 1e3, 3),
+                     "insert_us": round(im * 1e3, 3), "kv_bytes": kv}
+
+    # C4: 48 target layers (36 sliding-window, 12 global) + 6 draft layers at context 8192;
+    # one cycle = one fused insert + decode call per layer. Two copies of the cycle's layers
+    # are alternated so consecutive cycles do not find the K/V in the 256 MB Infinity Cache.
+    layers = [synth.c4_layer(i) for i in range(synth.C4_LAYERS + synth.C4_DRAFT_LAYERS)]
+    copies = [[layer_step(lay) for lay in layers] for _ in range(2)]
+    kv54 = sum(_visible_kv_bytes(lay, 1) for lay in layers)
+    kv48 = sum(_visible_kv_bytes(lay, 1) for lay in layers[:synth.C4_LAYERS])
+    which = [0]
+
+    def cycle_eager():
+        c = copies[which[0] % 2]
+        which[0] += 1
+        for gl in c:
+            gl.insert_decode(stream)
+
+    em, _ = _time_calls(cycle_eager, stream, max(20, iters // 4), 4)
+    graphs = []
+    for c in copies:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for gl in c:
+                gl.insert_decode()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # every replay must reproduce the eager outputs bit for bit (eager work in between)
+    for c, g in zip(copies, graphs):
+        with torch.cuda.stream(stream):
+            for gl in c:
+                gl.insert_decode(stream)
+        stream.synchronize()
+        ref = [gl.out.clone() for gl in c]
+        for _ in range(3):
+            for gl in c:
+                gl.out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert all(torch.equal(gl.out, r) for gl, r in zip(c, ref)), "graph replay differs from eager"
+            with torch.cuda.stream(stream):
+                c[0].decode(stream)
+            stream.synchronize()
+    def cycle_graph():
+        which[0] += 1
+        graphs[which[0] % 2].replay()
+
+    gm, _ = _time_calls(cycle_graph, stream, max(20, iters // 4), 4)
+    out["c4_cycle"] = {"layers": len(layers), "eager_us": round(em * 1e3, 2), "graph_us": round(gm * 1e3, 2),
+                       "graph_us_per_layer": round(gm * 1e3 / len(layers), 3), "kv_bytes_54_layers": kv54,
+                       "kv_bytes_48_layers": kv48, "graph_kv_gbs": round(kv54 / (gm * 1e-3) / 1e9, 1),
+                       "replays_checked": 6}
+    del copies, graphs
+    torch.cuda.empty_cache()
+
+    # C5: 32 sequences, 72/8 heads, contexts log-uniform in [1k, 128k], page 32, one pool
+    for q_len in (12, 1):
+        for dt in ("fp8_e4m3fn", "bf16"):
+            lay = synth.c5_layer(q_len=q_len, cache_dtype=dt)
+            fp8 = dt == "fp8_e4m3fn"
+            gl = layer_step(lay, fused=fp8)
+            dm, _ = _time_calls(lambda: gl.decode(stream), stream, max(20, iters // 4), 5)
+            kv = _visible_kv_bytes(lay, 1 if fp8 else 2)
+            rec = {"decode_us": round(dm * 1e3, 2), "kv_bytes": kv, "decode_kv_gbs": round(kv / (dm * 1e-3) / 1e9, 1),
+                   "layout": "5 (32-row kernel)" if fp8 else "3 (row-group kernel)"}
+            if fp8:
+                fm, _ = _time_calls(lambda: gl.insert_decode(stream), stream, max(20, iters // 4), 5)
+                rec["fused_step_us"] = round(fm * 1e3, 2)
+                rec["fused_kv_gbs"] = round(kv / (fm * 1e-3) / 1e9, 1)
+            out[f"c5_m{q_len}_{'fp8' if fp8 else 'bf16'}"] = rec
+            del gl
+            torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(seconds):
@@ -288,6 +418,8 @@ def main():
             if rr["fused_insert"]:
                 extra[f"{ctx}_p{bs}"]["fused_step_us"] = round(rr["fused_ms"] * 1e3, 3)
         line["ab"] = extra
+    if args.suite:
+        line["suite"] = run_suite(args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -692,37 +692,88 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     if (has_new(tb + kl)) patch(tb + kl, xa);
     qk(xa, sa);
   }
-  for (int i = 0; i < nsteps; ++i) {
+  // The barrier part of step i (every wave takes part in every step's barrier).
+  auto sync_step = [&](int i) {
     if (i + 1 < nsteps) {
       wait_steps<S::kPerWave, S::kDepth - 2>(min(nsteps - 2 - i, S::kDepth - 2));
       asm volatile("s_barrier" ::: "memory");
       if (i + S::kDepth < nsteps) issue(i + S::kDepth);
     }
-    if (i >= nfull) continue;  // wave-uniform: no tile of this wave at step i (barriers still counted)
-    const int tile = tb + KL * i + kl;
-    if (!interior(tile)) mask(tile, sa, xa);
-    uint32_t hw[RW][8];
-    float lt[RW];
-    if (i + 1 < nfull) {
-      read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xb);
-      if (has_new(tile + KL)) patch(tile + KL, xb);
-      // S^T of the next tile interleaved with this tile's probabilities
-      qk(xb, sb);
-#pragma unroll
-      for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
-    }
+  };
+  // probabilities of the current tile, the rare raise, then O^T += V^T P^T
+  auto finish_tile = [&](const TileRegs32<true>& xc, uint32_t (&hw)[RW][8], float (&lt)[RW], f32x16_t (&sc)[RW]) {
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      if (__builtin_amdgcn_ballot_w64(!(lt[r] <= kAcceptSum)) != 0) raise(r, sa[r], hw[r], lt[r]);
+      if (__builtin_amdgcn_ballot_w64(!(lt[r] <= kAcceptSum)) != 0) raise(r, sc[r], hw[r], lt[r]);
       lsum[r] += lt[r];
     }
-    pv(xa, hw);
-    xa = xb;
+    pv(xc, hw);
+  };
+  // Step i of a wave that has a tile at i + 1 too: S^T of the next tile and the
+  // probabilities of this one come in one straight-line block, so their MFMA and VALU work
+  // can interleave.
+  auto full_step = [&](int i, TileRegs32<true>& xc, TileRegs32<true>& xn, f32x16_t (&sc)[RW], f32x16_t (&sn)[RW]) {
+    sync_step(i);
+    const int tile = tb + KL * i + kl;
+    if (!interior(tile)) mask(tile, sc, xc);
+    read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xn);
+    if (has_new(tile + KL)) patch(tile + KL, xn);
+    uint32_t hw[RW][8];
+    float lt[RW];
+    qk(xn, sn);
 #pragma unroll
-    for (int r = 0; r < RW; ++r) sa[r] = sb[r];
+    for (int r = 0; r < RW; ++r) lt[r] = probs(sc[r], m_ref[r], hw[r]);
+    finish_tile(xc, hw, lt, sc);
+  };
+  // the wave's last tile
+  auto last_step = [&](int i, TileRegs32<true>& xc, f32x16_t (&sc)[RW]) {
+    sync_step(i);
+    const int tile = tb + KL * i + kl;
+    if (!interior(tile)) mask(tile, sc, xc);
+    uint32_t hw[RW][8];
+    float lt[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) lt[r] = probs(sc[r], m_ref[r], hw[r]);
+    finish_tile(xc, hw, lt, sc);
+  };
+  if constexpr (RW == 1) {
+    int i = 0;
+    for (; i + 1 < nfull; ++i) {
+      full_step(i, xa, xb, sa, sb);
+      xa = xb;
+      sa[0] = sb[0];
+    }
+    if (i < nfull) {
+      last_step(i, xa, sa);
+      ++i;
+    }
+    for (; i < nsteps; ++i) sync_step(i);  // no tile of this wave left (barriers still counted)
+  } else {
+    // Two row tiles per wave keep the step in one piece: the next tile's S^T and this
+    // tile's probabilities in separate blocks. (The straight-line form above gave wrong
+    // results with the AGPR accumulators on MI355X; kept out until its cause is known.)
+    for (int i = 0; i < nsteps; ++i) {
+      sync_step(i);
+      if (i >= nfull) continue;  // wave-uniform: no tile of this wave at step i
+      const int tile = tb + KL * i + kl;
+      if (!interior(tile)) mask(tile, sa, xa);
+      uint32_t hw[RW][8];
+      float lt[RW];
+      if (i + 1 < nfull) {
+        read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xb);
+        if (has_new(tile + KL)) patch(tile + KL, xb);
+        qk(xb, sb);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
+      }
+      finish_tile(xa, hw, lt, sa);
+      xa = xb;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) sa[r] = sb[r];
+    }
   }
 
   // ---- merge the KL key lanes of each row tile in a fixed order
