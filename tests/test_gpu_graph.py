@@ -1,0 +1,87 @@
+"""Graph capture of a multi-layer decode cycle: every entry point is capturable (device
+scalars, caller-owned workspaces, no allocation, no host synchronisation), each replay
+reproduces the eager outputs bit for bit, the inserted cache bytes stay those of the eager
+insert, and the launch counters count the captured launches once (at capture) and nothing
+per replay."""
+
+import pytest
+import torch
+
+from fp8_kv_paged_amd import fkv, synth
+from fp8_kv_paged_amd.layer import PagedLayer
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X")]
+
+
+def _cycle_layers():
+    """Sliding-window, global and draft layers of the 48 (+6) layer cycle (context 8192)."""
+    ids = [0, 1, 3, 7, 48, 53]
+    layers = []
+    for i in ids:
+        gl = PagedLayer(synth.c4_layer(i))
+        gl.prefill()
+        gl.stage_new_tokens()
+        layers.append(gl)
+    return layers
+
+
+def test_cycle_graph_replays_match_eager():
+    layers = _cycle_layers()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for gl in layers:
+            gl.insert_decode(stream)
+    stream.synchronize()
+    ref_out = [gl.out.clone() for gl in layers]
+    ref_k = [gl.k_pool.clone() for gl in layers]
+    ref_v = [gl.v_pool.clone() for gl in layers]
+    before = fkv.get_counters()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for gl in layers:
+            gl.insert_decode()
+    torch.cuda.synchronize()
+    mid = fkv.get_counters()
+    assert mid["insert_decode_launches"] == before["insert_decode_launches"] + len(layers)
+    for rep in range(3):
+        for gl in layers:
+            gl.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, gl in enumerate(layers):
+            assert torch.equal(gl.out, ref_out[j]), (rep, j)
+            assert torch.equal(gl.k_pool, ref_k[j]) and torch.equal(gl.v_pool, ref_v[j]), (rep, j)
+        # eager work between replays (another layer's decode on the side stream)
+        with torch.cuda.stream(stream):
+            layers[0].decode(stream)
+        stream.synchronize()
+    after = fkv.get_counters()
+    assert after["insert_decode_launches"] == mid["insert_decode_launches"]  # replays bypass the host
+    print(f"[graph] {len(layers)}-layer cycle: 3 replays equal to eager", flush=True)
+
+
+def test_decode_graph_with_split_merge_counters():
+    """A captured decode whose splits merge inside the kernel: the workspace counters return
+    to zero at the end of every replay, so replays stay equal to the eager call."""
+    lay = synth.c3_layer(8192, 64)
+    gl = PagedLayer(lay).build()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        gl.decode(stream)
+    stream.synchronize()
+    ref = gl.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        gl.decode()
+    torch.cuda.synchronize()
+    nws = fkv.decode_workspace_bytes(gl.cache, gl.ddesc)
+    ctl = lay.num_seqs * lay.num_kv_heads * 256
+    for rep in range(4):
+        gl.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gl.out, ref), rep
+        assert torch.count_nonzero(gl.workspace[nws - ctl:nws]).item() == 0, rep
