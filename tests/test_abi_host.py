@@ -147,6 +147,25 @@ def test_calls_fail_closed_without_touching_the_gpu():
     assert L.fkv_insert(ctypes.byref(c), dev, dev, dev, 4, dev, dev, None) == fkv.EINVAL
 
 
+def test_layout6_plan_rules():
+    """Layout 6 (two row tiles per wave): FP8 cache, at least two 32-row tiles, row groups
+    fixed at half the row tiles; its workspace equals layout 5's with the same row groups."""
+    c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
+    kw = dict(num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192)
+    assert _ws(c, layout=6, **kw) == _ws(c, layout=5, row_groups=2, **kw)
+    assert _ws(c, layout=6, q_len=6, **kw) == _ws(c, layout=5, row_groups=1, q_len=6, **kw)
+    for bad in (dict(layout=6, q_len=1), dict(layout=6, row_groups=1), dict(layout=6, row_groups=4)):
+        with pytest.raises(fkv.FkvError) as e:
+            _ws(c, **kw, **bad)
+        assert e.value.status == fkv.EUNSUPPORTED, bad
+    with pytest.raises(fkv.FkvError) as e:
+        _ws(_fake_cache(num_blocks=4096, bs=64, hkv=8, dt="bf16"), layout=6, **kw)
+    assert e.value.status == fkv.EUNSUPPORTED
+    with pytest.raises(fkv.FkvError) as e:
+        _ws(c, layout=7, **kw)
+    assert e.value.status == fkv.EINVAL
+
+
 def test_insert_decode_fails_closed_without_touching_the_gpu():
     L = fkv.lib()
     c = _fake_cache()
