@@ -69,6 +69,7 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
     return FKV_EINVAL;
   if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
   if (d->layout < 0 || d->layout > 6) return FKV_EINVAL;
+  if (d->row_exact && (d->split_tiles == 0 || d->split_tiles % 4 != 0)) return FKV_EINVAL;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
@@ -95,6 +96,9 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
   const bool fp8 = c->desc.cache_dtype == FKV_FP8_E4M3FN;
   const fkv::SplitShapeInfo sh = fkv::split_shape(nt, d->layout, fp8);
   p->row_groups = 1;
+  p->key_lanes = 0;
+  p->align_splits = 0;
+  if (d->row_exact && (!fp8 || (d->layout != 0 && d->layout != 5))) return FKV_EUNSUPPORTED;
   int64_t tps = d->split_tiles;
   if (sh.groups_per_cu == -2 || sh.groups_per_cu == -3) {
     // 32-row kernel: the rows_pad = 32 * rt_total packed rows of a KV head are cut into RG
@@ -118,9 +122,16 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
       if (d->row_groups != 0 && d->row_groups != rt_total / 2) return FKV_EUNSUPPORTED;
       rg = rt_total / 2;
     }
+    if (d->row_exact) {
+      // row-exact mode: four key lanes whatever the rows (one or two row tiles per work group)
+      if (d->row_groups == 0) rg = rt_total >= 2 ? rt_total / 2 : 1;
+      if (rt_total / rg > 2) return FKV_EUNSUPPORTED;
+      p->align_splits = 1;
+    }
     if (rg > rt_total) return FKV_EUNSUPPORTED;
     p->row_groups = rg;
-    const int kl = sh.groups_per_cu == -3 ? 4 : 8 / (rt_total / rg);
+    const int kl = (sh.groups_per_cu == -3 || d->row_exact) ? 4 : 8 / (rt_total / rg);
+    p->key_lanes = kl;
     if (tps == 0) {
       const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * rg));
       tps = (tiles_max + splits - 1) / splits;
@@ -155,7 +166,8 @@ int plan_decode(const fkv_cache* c, const fkv_decode_desc* d, fkv::DecodePlan* p
     if (sh.ntw <= 2) tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
   }
   if (sh.ntw <= 2 && tps > fkv::kMaxDmaSplitTiles) return FKV_EUNSUPPORTED;
-  const int64_t max_splits = (tiles_max + tps - 1) / tps;
+  // aligned splits (row-exact mode) can straddle one more split boundary inside a window
+  const int64_t max_splits = (tiles_max + tps - 1) / tps + (p->align_splits && d->window_left >= 0 ? 1 : 0);
   if (max_splits > fkv::kMaxSplits) return FKV_EUNSUPPORTED;
   p->tiles_per_split = (int)tps;
   p->max_splits = (int)max_splits;
@@ -298,6 +310,8 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   a.max_seq_len = desc->max_seq_len;
   a.rows_pad = p.rows_pad;
   a.row_groups = p.row_groups;
+  a.key_lanes = p.key_lanes;
+  a.align_splits = p.align_splits;
   a.softmax_scale = desc->softmax_scale;
   bool combined = false;
   const hipError_t e = fkv::launch_decode(a, fkv::split_shape(p.nt, p.layout, fp8), fp8, static_cast<hipStream_t>(stream),

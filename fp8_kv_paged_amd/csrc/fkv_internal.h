@@ -36,6 +36,8 @@ struct DecodePlan {
   size_t ws_ml_bytes;  // fp32 (m, l) per partial row
   size_t ws_ctl_bytes; // in-kernel split merge: 256 bytes of counters and claim bits per pair
   int fused_combine;   // layout 5 with the whole grid resident: splits merged inside the kernel
+  int key_lanes;       // 32-row kernel: key lanes per work group
+  int align_splits;    // 32-row kernel, row-exact mode: split boundaries at absolute tile indices
   int xcd_pairs;       // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   size_t ws_bytes;     // total, 256-byte aligned pieces
 };
@@ -59,6 +61,8 @@ struct DecodeArgs {
   int32_t row_groups;  // row-group kernel: groups of 16*ntw packed rows
   int32_t xcd_pairs;   // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   int32_t fused_combine;  // 32-row kernel: merge the splits inside the kernel (no combine launch)
+  int32_t key_lanes;      // 32-row kernel: key lanes per work group
+  int32_t align_splits;   // 32-row kernel: splits start at multiples of tiles_per_split (row-exact mode)
   float softmax_scale;
 };
 
@@ -104,7 +108,7 @@ inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
 hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
 // 32-row tile kernel: rt row tiles of 32 per work group (1, 2 or 4) and rw per wave (layout 5:
 // 1; layout 6: 2 with rt = 2), FP8 cache only.
-hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, bool fp8, hipStream_t stream);
+hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, int kl, bool fp8, hipStream_t stream);
 // Wide split kernel (layout 4): ntw 16-row tiles per row half.
 hipError_t launch_wide(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
 // Merges the wide kernel's lane-layout split partials into out.

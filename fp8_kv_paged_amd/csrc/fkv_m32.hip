@@ -319,7 +319,10 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   const int t_first = lo_u / kTile;
   const int t_end = L > 0 ? (L + kTile - 1) / kTile : 0;
   const int ntiles = max(0, t_end - t_first);
-  const int nsplit = (ntiles + tps - 1) / tps;
+  // splits start at t_first, or (row-exact mode) at multiples of tps so that a key meets the
+  // same split and key lane in every call
+  const int t_base = a.align_splits ? t_first / tps * tps : t_first;
+  const int nsplit = (t_end - t_base + tps - 1) / tps;
   if (ntiles == 0) {
     // no visible key for any row: split 0, row group 0 writes the rows as zeros
     if (s == 0 && rg == 0) {
@@ -339,7 +342,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   const int group_wgs = nsplit * RG;  // work groups that write partials of this pair
   if (fused && threadIdx.x == 0)
     __hip_atomic_fetch_add(&ctl[kCtlStarted], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int tb = t_first + s * tps;
+  const int tb = t_base + s * tps;
   const int te = min(tb + tps, t_end);
   if (wl >= 0) {
     lb0 = tb >> bshift;
@@ -1032,15 +1035,14 @@ static hipError_t launch_m32_t(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, bool fp8, hipStream_t stream) {
+hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, int kl, bool fp8, hipStream_t stream) {
   if (!fp8) return hipErrorInvalidValue;
-  if (rw == 2) return rt == 2 ? launch_m32_t<2, 4, 2>(a, stream) : hipErrorInvalidValue;
-  switch (rt) {
-    case 1: return launch_m32_t<1, 8, 1>(a, stream);
-    case 2: return launch_m32_t<2, 4, 1>(a, stream);
-    case 4: return launch_m32_t<4, 2, 1>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (rw == 2) return (rt == 2 && kl == 4) ? launch_m32_t<2, 4, 2>(a, stream) : hipErrorInvalidValue;
+  if (rt == 1 && kl == 8) return launch_m32_t<1, 8, 1>(a, stream);
+  if (rt == 1 && kl == 4) return launch_m32_t<1, 4, 1>(a, stream);  // one row tile, four waves
+  if (rt == 2 && kl == 4) return launch_m32_t<2, 4, 1>(a, stream);
+  if (rt == 4 && kl == 2) return launch_m32_t<4, 2, 1>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fkv

@@ -42,7 +42,8 @@ class DecodeDesc(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("window_left", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("out_dtype", ctypes.c_int32),
-                ("split_tiles", ctypes.c_int32), ("layout", ctypes.c_int32), ("row_groups", ctypes.c_int32)]
+                ("split_tiles", ctypes.c_int32), ("layout", ctypes.c_int32), ("row_groups", ctypes.c_int32),
+                ("row_exact", ctypes.c_int32)]
 
 
 class Counters(ctypes.Structure):
@@ -145,9 +146,10 @@ def insert(cache, k, v, slot_mapping, k_scale, v_scale, stream=None):
 
 
 def make_decode_desc(num_seqs, q_len, num_q_heads, max_blocks_per_seq, max_seq_len, window_left=-1,
-                     softmax_scale=1.0 / math.sqrt(HEAD_DIM), split_tiles=0, layout=0, row_groups=0):
+                     softmax_scale=1.0 / math.sqrt(HEAD_DIM), split_tiles=0, layout=0, row_groups=0, row_exact=0):
     return DecodeDesc(int(num_seqs), int(q_len), int(num_q_heads), int(max_blocks_per_seq), int(max_seq_len),
-                      int(window_left), float(softmax_scale), OUT_F32, int(split_tiles), int(layout), int(row_groups))
+                      int(window_left), float(softmax_scale), OUT_F32, int(split_tiles), int(layout), int(row_groups),
+                      int(row_exact))
 
 
 def decode_workspace_bytes(cache, desc):

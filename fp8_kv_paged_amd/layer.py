@@ -22,7 +22,7 @@ def to_dev_bits(bits, device):
 
 
 class PagedLayer:
-    def __init__(self, lay, device="cuda", poison=True, split_tiles=0, layout=0, row_groups=0):
+    def __init__(self, lay, device="cuda", poison=True, split_tiles=0, layout=0, row_groups=0, row_exact=0):
         self.lay = lay
         self.device = device
         self.desc = fkv.make_cache_desc(lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.cache_dtype)
@@ -37,7 +37,8 @@ class PagedLayer:
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(lay.seq_lens)).to(device)
         self.max_seq_len = int(max(1, lay.seq_lens.max())) if lay.num_seqs else 1
         self.ddesc = fkv.make_decode_desc(lay.num_seqs, lay.q_len, lay.num_q_heads, lay.max_blocks, self.max_seq_len,
-                                          lay.window_left, lay.softmax_scale, split_tiles, layout, row_groups)
+                                          lay.window_left, lay.softmax_scale, split_tiles, layout, row_groups,
+                                          row_exact)
         self.q = to_dev_bits(lay.q_bits(), device)
         self.out = torch.empty((lay.num_seqs, lay.q_len, lay.num_q_heads, HEAD_DIM), dtype=torch.float32,
                                device=device)

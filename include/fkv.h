@@ -162,6 +162,15 @@ typedef struct fkv_decode_desc {
                                   or 4, at most the number of 32-row tiles; 0 = automatic);
                                   layout 6: 0 or the number of 32-row tiles / 2 (else
                                   FKV_EUNSUPPORTED); ignored by the other layouts           */
+  int32_t row_exact;           /* nonzero: row-exact mode (layout 0 or 5, FP8 cache, else
+                                  FKV_EUNSUPPORTED; split_tiles > 0 and a multiple of 4,
+                                  else FKV_EINVAL). A query row's output then depends only on
+                                  its own query, its position and the cache: calls with equal
+                                  split_tiles give bitwise-equal rows, e.g. row i of a q_len =
+                                  12 call equals a q_len = 1 call at seq_len L - 12 + i + 1
+                                  ([P3] "Result progression and what actually worked": a
+                                  verifier with M=1 numerical lanes; "Numerical width is a
+                                  contract, not just a tensor shape": row-wise lanes)     */
 } fkv_decode_desc;
 
 /*

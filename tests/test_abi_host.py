@@ -166,6 +166,30 @@ def test_layout6_plan_rules():
     assert e.value.status == fkv.EINVAL
 
 
+def test_row_exact_plan_rules():
+    """Row-exact mode: explicit split_tiles (a multiple of 4), FP8 cache, layout 0 or 5, at most two
+    row tiles per work group."""
+    c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
+    kw = dict(num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192)
+    assert _ws(c, row_exact=1, split_tiles=16, **kw) == _ws(c, row_groups=2, split_tiles=16, **kw)
+    assert _ws(c, row_exact=1, split_tiles=16, q_len=1, **kw) > 0
+    for bad, code in ((dict(split_tiles=0), fkv.EINVAL), (dict(split_tiles=6), fkv.EINVAL),
+                      (dict(split_tiles=8, layout=3), fkv.EUNSUPPORTED),
+                      (dict(split_tiles=8, layout=6), fkv.EUNSUPPORTED),
+                      (dict(split_tiles=8, row_groups=1), fkv.EUNSUPPORTED)):
+        with pytest.raises(fkv.FkvError) as e:
+            _ws(c, row_exact=1, **kw, **bad)
+        assert e.value.status == code, bad
+    with pytest.raises(fkv.FkvError) as e:
+        _ws(_fake_cache(num_blocks=4096, bs=64, hkv=8, dt="bf16"), row_exact=1, split_tiles=8, **kw)
+    assert e.value.status == fkv.EUNSUPPORTED
+    # sliding windows: aligned splits may straddle one more boundary
+    # (5 -> 6 splits of partials; the 256 bytes of merge counters per pair do not scale)
+    ctl = 8 * 256
+    sw = _ws(c, row_exact=1, split_tiles=4, window_left=511, **kw)
+    assert sw - ctl == (_ws(c, row_groups=2, split_tiles=4, window_left=511, **kw) - ctl) * 6 // 5
+
+
 def test_insert_decode_fails_closed_without_touching_the_gpu():
     L = fkv.lib()
     c = _fake_cache()

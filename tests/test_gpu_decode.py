@@ -249,3 +249,35 @@ def test_two_row_tiles_per_wave_is_bitwise_layout5(name, make, q_len, split_tile
     torch.cuda.synchronize()
     assert torch.equal(out5, out6), name
     _check(lay, out6, label=f"{name} layout 6 split_tiles {split_tiles}")
+
+
+@pytest.mark.parametrize("window_left,L", [(-1, 3000), (511, 2000), (63, 700), (-1, 40)])
+@pytest.mark.parametrize("split_tiles", [4, 8])
+def test_row_exact_rows_equal_single_query_calls(window_left, L, split_tiles):
+    """Row-exact mode: row i of an M=12 call is bitwise equal to a q1 call at seq_len
+    L - 12 + i + 1 (same cache, same split_tiles)."""
+    M = 12
+    lay = synth.tiny_layer(131 + L + window_left, [L], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=M,
+                           window_left=window_left, outlier_rate=0.01)
+    gl = PagedLayer(lay, split_tiles=split_tiles, row_exact=1).build()
+    out = gl.decode().clone()
+    for i in range(M):
+        d1 = fkv.make_decode_desc(1, 1, 18, lay.max_blocks, L, window_left, lay.softmax_scale,
+                                  split_tiles=split_tiles, row_exact=1)
+        q1 = to_dev_bits(lay.q_bits()[:, i:i + 1], "cuda")
+        o1 = torch.empty((1, 1, 18, 128), dtype=torch.float32, device="cuda")
+        sl = torch.tensor([L - M + i + 1], dtype=torch.int32, device="cuda")
+        ws = torch.zeros((max(16, fkv.decode_workspace_bytes(gl.cache, d1)),), dtype=torch.uint8, device="cuda")
+        fkv.decode_attn(gl.cache, d1, q1, gl.block_table, sl, gl.k_scale, gl.v_scale, o1, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0, 0], out[0, i]), (i, float((o1[0, 0] - out[0, i]).abs().max()))
+    _check(lay, out, label=f"row exact L {L} window {window_left} split_tiles {split_tiles}")
+
+
+def test_row_exact_full_layer():
+    """Row-exact mode on the 72/8-head layer at 8k (two row tiles per work group, four key lanes)."""
+    lay = synth.c3_layer(8192, 64)
+    gl = PagedLayer(lay, split_tiles=16, row_exact=1).build()
+    out = gl.decode()
+    torch.cuda.synchronize()
+    _check(lay, out, label="c3_8k_p64 row exact")

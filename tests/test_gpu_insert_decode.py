@@ -110,6 +110,11 @@ def test_sliding_windows(window_left):
     _fused_vs_separate(lay, f"window {window_left}")
 
 
+def test_row_exact_mode():
+    lay = synth.tiny_layer(419, [3000, 257, 12, 5], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=12)
+    _fused_vs_separate(lay, "row exact", split_tiles=8, row_exact=1)
+
+
 def test_single_query():
     lay = synth.tiny_layer(413, [1, 32, 33, 300], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=1)
     _fused_vs_separate(lay, "q1")
