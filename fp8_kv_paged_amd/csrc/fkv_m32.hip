@@ -1,4 +1,5 @@
-// Paged GQA decode attention, 32-row tile kernel (layout 5).
+// Paged GQA decode attention, 32-row tile kernel (layouts 5 and 6), with the new tokens'
+// cache insertion optionally fused into its prologue.
 //
 // Operation: exact q1 / M12 paged attention over the calibrated FP8 cache ("Laguna S 2.1
 // INT4 -- calibrated FP8 KV on Intel B70", sections Contract and "Initial optimization
@@ -6,23 +7,25 @@
 // KV -- replicated embedding win, page-32 build, and host boundary", section "Page-32
 // attention experiment").
 //
-// Work decomposition. One work group per (sequence, KV head, split) holds every packed
-// query row of the KV head (G*M rows, at most 128), so each K/V byte of the split is read
-// from memory exactly once. The rows are cut into RT tiles of 32 and the split's 32-key
-// tiles into KL key lanes: wave w computes row tile w % RT of every KL-th tile. Waves w
-// and w + 4 share a SIMD, so each SIMD holds one row tile (balanced) and two waves whose
-// MFMA and softmax phases overlap.
+// Work decomposition. One work group per (sequence, KV head, split, row group): RT row
+// tiles of 32 packed query rows (G*M rows of the KV head, at most 128, over the row groups)
+// and the split's 32-key tiles in KL key lanes; each wave holds RW row tiles of one key
+// lane. Layout 5 (RW = 1): eight waves, waves w and w + 4 on one SIMD, so each SIMD runs two
+// waves whose MFMA and softmax phases overlap. Layout 6 (RW = 2): four waves, one per SIMD,
+// every converted K/V operand feeding two MFMAs.
 //   * All waves fill an LDS ring of kDepth steps (a step = the KL tiles computed
 //     together) with global_load_lds, kDepth - 1 steps ahead; one barrier per step
 //     publishes a step and frees the slot read in the previous one. Each chunk is fetched
 //     in the order the MFMA operands want it, so the LDS reads are lane-contiguous.
 //   * S^T = K Q^T on MFMA 32x32x16 bf16 (fp8 -> bf16 exact), online softmax in the log2
 //     domain against a lazily raised per-row reference, O^T += V^T P^T on MFMA 32x32x16
-//     f16 (fp8 -> f16 exact, P rounded to the nearest f16). The S^T products of tile i+1 are issued in
-//     the same block as the probabilities of tile i, so MFMA and VALU work interleave.
+//     f16 (fp8 -> f16 exact, P rounded to the nearest f16). The S^T products of tile i+1
+//     are issued in the same block as the probabilities of tile i, so MFMA and VALU work
+//     interleave.
 //   * After the loop the KL key lanes of a row tile merge through LDS in a fixed order
-//     and the group writes final rows (one split) or an fp32 partial (m, l, O) that
-//     decode_combine_kernel merges over splits in split order.
+//     and the group writes final rows (one split) or an fp32 partial (m, l, O). The
+//     partials of a (sequence, KV head) are merged in split order inside this kernel when
+//     the grid fits on the chip, else by decode_combine_kernel.
 //   * Work groups are numbered so that every split of one (sequence, KV head) runs on the
 //     same XCD (ids congruent mod 8) when there are at least 8 such pairs.
 //
