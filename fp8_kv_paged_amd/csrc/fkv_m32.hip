@@ -65,8 +65,12 @@ struct M32Shape {
   static constexpr int kPerWave = KL * kChunks / kWaves;         // DMA instructions per wave per step
   static constexpr int kDepth = (128 * 1024) / kStepBytes < 8 ? (128 * 1024) / kStepBytes : 8;
   static constexpr int kRing = kDepth * kStepBytes;
-  static constexpr int kXch = kWaves * RW * 64 * 64 * 4;         // merge exchange: 64 floats per lane per row tile
-  static constexpr int kBody = kRing > kXch ? kRing : kXch;
+  // key-lane merge: each owner receives (KL - 1) sources x (16 / KL) quads x 64 lanes of
+  // f32x4 per row tile; the merged rows are staged in an area of their own
+  static constexpr int kXch = RT * (KL - 1) * 16 * 64 * 16;
+  static constexpr int kStageStride = kHeadDim + 4;                 // floats per staged row (conflict-free)
+  static constexpr int kStage = 32 * RT * kStageStride * 4;
+  static constexpr int kBody = kRing > kXch + kStage ? kRing : kXch + kStage;
   static_assert(kDepth >= 2, "ring of at least two steps");
   static_assert((kDepth - 2) * kPerWave <= 63, "vmcnt range");
   static_assert(KL * kChunks % kWaves == 0, "DMA chunks split evenly over the waves");
@@ -782,11 +786,24 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     }
   }
 
-  // ---- merge the KL key lanes of each row tile in a fixed order
+  // ---- merge the KL key lanes of each row tile in a fixed order. Every wave writes its
+  // (m, l) and its unscaled accumulators of the groups other key lanes own as soon as its
+  // loop ends; after one barrier each owner rescales and sums its groups over the key lanes
+  // in lane order and stages the merged rows.
   if constexpr (RW == 2) {
     acc_fence32(o[0]);
     acc_fence32(o[1]);
   }
+  // Output group gi = 4a + i holds dims 64a + 16i + 8hh + 0..7: elements 4i..4i+3 of d-tiles
+  // 2a and 2a + 1. Key lane kl owns groups kl*GPK .. +GPK-1 and receives them from the others.
+  constexpr int kGpk = 8 / KL;
+  // [owner][row tile][source, owner skipped][kGpk*2 quads][64 lanes][4 floats]: 16-byte,
+  // lane-contiguous accesses
+  f32x4_t* xch = reinterpret_cast<f32x4_t*>(body);
+  auto xidx = [&](int owner, int rt, int src, int f4) -> int {
+    const int slot = src < owner ? src : src - 1;
+    return (((owner * RT + rt) * (KL - 1) + slot) * (kGpk * 2) + f4) * 64 + lane;
+  };
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const float lrow = pair_sum(lsum[r]);
@@ -794,30 +811,6 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       sm_m[kl * kRows + rl[r]] = m_ref[r];
       sm_l[kl * kRows + rl[r]] = lrow;
     }
-  }
-  __syncthreads();  // also: every ring read is done, the ring area is free
-  float Mrow[RW], Lrow[RW], asf[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    Mrow[r] = sm_m[rl[r]];
-#pragma unroll
-    for (int k = 1; k < KL; ++k) Mrow[r] = fmaxf(Mrow[r], sm_m[k * kRows + rl[r]]);
-    Lrow[r] = 0.f;
-#pragma unroll
-    for (int k = 0; k < KL; ++k)
-      Lrow[r] += sm_l[k * kRows + rl[r]] * __builtin_amdgcn_exp2f(sm_m[k * kRows + rl[r]] - Mrow[r]);
-    asf[r] = __builtin_amdgcn_exp2f(m_ref[r] - Mrow[r]);
-  }
-  // Output group gi = 4a + i holds dims 64a + 16i + 8hh + 0..7: elements 4i..4i+3 of d-tiles
-  // 2a and 2a + 1. Key lane kl owns groups kl*GPK .. +GPK-1 and receives them from the others.
-  constexpr int kGpk = 8 / KL;
-  // [owner][row tile][source][kGpk*2 quads][64 lanes][4 floats]: 16-byte, lane-contiguous accesses
-  f32x4_t* xch = reinterpret_cast<f32x4_t*>(body);
-  auto xidx = [&](int owner, int rt, int src, int f4) -> int {
-    return (((owner * RT + rt) * KL + src) * (kGpk * 2) + f4) * 64 + lane;
-  };
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int gi = 0; gi < 8; ++gi) {
       const int owner = gi / kGpk;
@@ -827,57 +820,60 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       for (int bb = 0; bb < 2; ++bb) {
         const f32x16_t& acc = o[r][2 * aa + bb];
         xch[xidx(owner, rtg * RW + r, kl, (gi % kGpk) * 2 + bb)] =
-            f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf[r];
+            f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]};
       }
     }
-  __syncthreads();
+  }
+  __syncthreads();  // also: every ring read is done, the ring area is free
   const bool direct = (nsplit == 1);
   const float vsc = *a.v_scale;
   const int64_t part = ((int64_t)b * a.num_kv_heads + g) * a.max_splits + s;
-  // The owners sum their groups over the key lanes in lane order, then the merged rows are
-  // staged row-major in LDS (rows padded to kStageStride floats: conflict-free) so that the
-  // group's stores write whole contiguous rows.
-  constexpr int kStageStride = kHeadDim + 4;
-  float o8s[RW][kGpk][8];
+  // The merged rows are staged row-major in LDS (rows padded to kStageStride floats:
+  // conflict-free) so that the group's stores write whole contiguous rows.
+  constexpr int kStageStride = S::kStageStride;
+  float* stage = reinterpret_cast<float*>(body + S::kXch);  // [kRows][kStageStride]
+  __shared__ float sm_row[2 * kRows];                       // merged (M, L) per row
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+  for (int r = 0; r < RW; ++r) {
+    // weight of key lane k: 2^(m_k - M); the lane's own weight scales its accumulators
+    float ew[KL];
+    float Mrow = sm_m[rl[r]];
+#pragma unroll
+    for (int k = 1; k < KL; ++k) Mrow = fmaxf(Mrow, sm_m[k * kRows + rl[r]]);
+    float Lrow = 0.f;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      ew[k] = __builtin_amdgcn_exp2f(sm_m[k * kRows + rl[r]] - Mrow);
+      Lrow += sm_l[k * kRows + rl[r]] * ew[k];
+    }
 #pragma unroll
     for (int gi = 0; gi < 8; ++gi) {
       // compile-time group index (the accumulators are only indexed by constants)
       if (gi / kGpk != kl) continue;
       const int gl = gi % kGpk;
       const int aa = gi >> 2, ii = gi & 3;
+      float o8[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o8s[r][gl][e] = 0.f;
+      for (int e = 0; e < 8; ++e) o8[e] = 0.f;
 #pragma unroll
       for (int src = 0; src < KL; ++src) {
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
           const f32x16_t& acc = o[r][2 * aa + bb];
-          const f32x4_t val = (src == kl)
-                                  ? f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]} * asf[r]
-                                  : xch[xidx(kl, rtg * RW + r, src, gl * 2 + bb)];
+          const f32x4_t val = (src == kl) ? f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]}
+                                          : xch[xidx(kl, rtg * RW + r, src, gl * 2 + bb)];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) o8s[r][gl][2 * k + bb] += val[k];
+          for (int k = 0; k < 4; ++k) o8[2 * k + bb] += val[k] * ew[src];
         }
       }
-    }
-  float* stage = reinterpret_cast<float*>(body);  // [kRows][kStageStride], over the exchange area
-  float* sm_row = sm_ml;                          // merged (M, L) per row, over the per-lane (m, l)
-  __syncthreads();  // every exchange and (m, l) read is done
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-#pragma unroll
-    for (int gl = 0; gl < kGpk; ++gl) {
-      const int gi = kl * kGpk + gl;
       const int d0 = 64 * (gi >> 2) + 16 * (gi & 3) + 8 * hh;
       float* st = stage + rl[r] * kStageStride + d0;
-      *reinterpret_cast<f32x4_t*>(st) = f32x4_t{o8s[r][gl][0], o8s[r][gl][1], o8s[r][gl][2], o8s[r][gl][3]};
-      *reinterpret_cast<f32x4_t*>(st + 4) = f32x4_t{o8s[r][gl][4], o8s[r][gl][5], o8s[r][gl][6], o8s[r][gl][7]};
+      *reinterpret_cast<f32x4_t*>(st) = f32x4_t{o8[0], o8[1], o8[2], o8[3]};
+      *reinterpret_cast<f32x4_t*>(st + 4) = f32x4_t{o8[4], o8[5], o8[6], o8[7]};
     }
     if (kl == 0 && hh == 0) {
-      sm_row[rl[r]] = Mrow[r];
-      sm_row[kRows + rl[r]] = Lrow[r];
+      sm_row[rl[r]] = Mrow;
+      sm_row[kRows + rl[r]] = Lrow;
     }
   }
   __syncthreads();
