@@ -86,13 +86,40 @@ struct M32Shape {
 __device__ __forceinline__ void pv32_f16(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
 }
-// The same product with the accumulator pinned to AGPRs (two row tiles per wave: 128
-// accumulators that would not fit beside the operands in the 256 VGPRs). Only inline asm
-// touches the AGPR copy, so the asm carries the wait states the hazard recognizer cannot
-// see: two after a VALU write of a source VGPR. Back-to-back MFMAs on one accumulator need
-// none.
-__device__ __forceinline__ void pv32_f16_agpr(f32x16_t& acc, const f16x8_t& a, const f16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+// With two row tiles per wave the 128 accumulators would not fit beside the operands in
+// the 256 VGPRs: they live in AGPRs and only inline asm touches them. The asm carries the
+// wait states the hazard recognizer cannot see: two after a VALU write of a source
+// register; back-to-back MFMAs on one accumulator need none.
+// All 16 P.V MFMAs of one tile for two row tiles in one asm block, accumulators in AGPRs:
+// the compiler can put no code between them (a register copy of an accumulator while an MFMA
+// writing it is in flight would read a stale value; the hazard recognizer cannot see into
+// asm), and the trailing 24 wait states let every later instruction read the results. Per
+// accumulator the products come in the order of pv32_f16: key half 0, then key half 1.
+__device__ __forceinline__ void pv32_f16_agpr_rw2(f32x16_t (&o0)[4], f32x16_t (&o1)[4], const f16x8_t (&va)[4],
+                                                  const f16x8_t (&vb)[4], const f16x8_t& p00, const f16x8_t& p01,
+                                                  const f16x8_t& p10, const f16x8_t& p11) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_f16 %0, %8, %16, %0\n\t"
+      "v_mfma_f32_32x32x16_f16 %4, %8, %18, %4\n\t"
+      "v_mfma_f32_32x32x16_f16 %0, %12, %17, %0\n\t"
+      "v_mfma_f32_32x32x16_f16 %4, %12, %19, %4\n\t"
+      "v_mfma_f32_32x32x16_f16 %1, %9, %16, %1\n\t"
+      "v_mfma_f32_32x32x16_f16 %5, %9, %18, %5\n\t"
+      "v_mfma_f32_32x32x16_f16 %1, %13, %17, %1\n\t"
+      "v_mfma_f32_32x32x16_f16 %5, %13, %19, %5\n\t"
+      "v_mfma_f32_32x32x16_f16 %2, %10, %16, %2\n\t"
+      "v_mfma_f32_32x32x16_f16 %6, %10, %18, %6\n\t"
+      "v_mfma_f32_32x32x16_f16 %2, %14, %17, %2\n\t"
+      "v_mfma_f32_32x32x16_f16 %6, %14, %19, %6\n\t"
+      "v_mfma_f32_32x32x16_f16 %3, %11, %16, %3\n\t"
+      "v_mfma_f32_32x32x16_f16 %7, %11, %18, %7\n\t"
+      "v_mfma_f32_32x32x16_f16 %3, %15, %17, %3\n\t"
+      "v_mfma_f32_32x32x16_f16 %7, %15, %19, %7\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+a"(o0[0]), "+a"(o0[1]), "+a"(o0[2]), "+a"(o0[3]), "+a"(o1[0]), "+a"(o1[1]), "+a"(o1[2]), "+a"(o1[3])
+      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "v"(p00),
+        "v"(p01), "v"(p10), "v"(p11));
 }
 // Orders every later access of a row tile's AGPR accumulators after the MFMAs in flight on
 // them (a 32x32 MFMA result may be read by other instructions only some passes after the
@@ -577,25 +604,29 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       P0[r] = __builtin_bit_cast(f16x8_t, u32x4_t{hw[r][0], hw[r][1], hw[r][2], hw[r][3]});
       P1[r] = __builtin_bit_cast(f16x8_t, u32x4_t{hw[r][4], hw[r][5], hw[r][6], hw[r][7]});
     }
+    if constexpr (RW == 2) {
+      f16x8_t va[4], vb[4];  // d-tile 2a+b: key half 0, key half 1
 #pragma unroll
-    for (int aa = 0; aa < 2; ++aa)
+      for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        const u32x4_t& v0 = x.v[aa];
-        const u32x4_t& v1 = x.v[2 + aa];
-        const f16x8_t va = fp8x8_to_f16x8(v0[2 * bb], v0[2 * bb + 1]);
-        const f16x8_t vb = fp8x8_to_f16x8(v1[2 * bb], v1[2 * bb + 1]);
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-          if constexpr (RW == 2) {
-            pv32_f16_agpr(o[r][2 * aa + bb], va, P0[r]);
-            pv32_f16_agpr(o[r][2 * aa + bb], vb, P1[r]);
-          } else {
-            pv32_f16(o[r][2 * aa + bb], va, P0[r]);
-            pv32_f16(o[r][2 * aa + bb], vb, P1[r]);
-          }
+        for (int bb = 0; bb < 2; ++bb) {
+          va[2 * aa + bb] = fp8x8_to_f16x8(x.v[aa][2 * bb], x.v[aa][2 * bb + 1]);
+          vb[2 * aa + bb] = fp8x8_to_f16x8(x.v[2 + aa][2 * bb], x.v[2 + aa][2 * bb + 1]);
         }
-      }
+      pv32_f16_agpr_rw2(o[0], o[RW - 1], va, vb, P0[0], P1[0], P0[RW - 1], P1[RW - 1]);
+    } else {
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const u32x4_t& v0 = x.v[aa];
+          const u32x4_t& v1 = x.v[2 + aa];
+          const f16x8_t va = fp8x8_to_f16x8(v0[2 * bb], v0[2 * bb + 1]);
+          const f16x8_t vb = fp8x8_to_f16x8(v1[2 * bb], v1[2 * bb + 1]);
+          pv32_f16(o[0][2 * aa + bb], va, P0[0]);
+          pv32_f16(o[0][2 * aa + bb], vb, P1[0]);
+        }
+    }
   };
 
   // ---- fused insert ("Laguna S 2.1 INT4 -- calibrated FP8 KV on Intel B70", section "Initial
@@ -746,45 +777,18 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     for (int r = 0; r < RW; ++r) lt[r] = probs(sc[r], m_ref[r], hw[r]);
     finish_tile(xc, hw, lt, sc);
   };
-  if constexpr (RW == 1) {
-    int i = 0;
-    for (; i + 1 < nfull; ++i) {
-      full_step(i, xa, xb, sa, sb);
-      xa = xb;
-      sa[0] = sb[0];
-    }
-    if (i < nfull) {
-      last_step(i, xa, sa);
-      ++i;
-    }
-    for (; i < nsteps; ++i) sync_step(i);  // no tile of this wave left (barriers still counted)
-  } else {
-    // Two row tiles per wave keep the step in one piece: the next tile's S^T and this
-    // tile's probabilities in separate blocks. (The straight-line form above gave wrong
-    // results with the AGPR accumulators on MI355X; kept out until its cause is known.)
-    for (int i = 0; i < nsteps; ++i) {
-      sync_step(i);
-      if (i >= nfull) continue;  // wave-uniform: no tile of this wave at step i
-      const int tile = tb + KL * i + kl;
-      if (!interior(tile)) mask(tile, sa, xa);
-      uint32_t hw[RW][8];
-      float lt[RW];
-      if (i + 1 < nfull) {
-        read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xb);
-        if (has_new(tile + KL)) patch(tile + KL, xb);
-        qk(xb, sb);
+  int i = 0;
+  for (; i + 1 < nfull; ++i) {
+    full_step(i, xa, xb, sa, sb);
+    xa = xb;
 #pragma unroll
-        for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < RW; ++r) lt[r] = probs(sa[r], m_ref[r], hw[r]);
-      }
-      finish_tile(xa, hw, lt, sa);
-      xa = xb;
-#pragma unroll
-      for (int r = 0; r < RW; ++r) sa[r] = sb[r];
-    }
+    for (int r = 0; r < RW; ++r) sa[r] = sb[r];
   }
+  if (i < nfull) {
+    last_step(i, xa, sa);
+    ++i;
+  }
+  for (; i < nsteps; ++i) sync_step(i);  // no tile of this wave left (barriers still counted)
 
   // ---- merge the KL key lanes of each row tile in a fixed order. Every wave writes its
   // (m, l) and its unscaled accumulators of the groups other key lanes own as soon as its
