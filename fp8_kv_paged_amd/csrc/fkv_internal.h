@@ -9,6 +9,7 @@ namespace fkv {
 constexpr int kWaves = 4;        // waves per decode work group
 constexpr int kMaxSplits = 512;  // split-KV partials per (sequence, KV head) the combine can merge
 constexpr int kMaxDmaSplitTiles = 128;  // 32-key tiles per split of the LDS-pipelined kernels
+constexpr int kFastMergeSplits = 16;    // 32-row kernel: splits one thread merges with all loads in flight
 
 struct InsertArgs {
   const uint16_t* k;

@@ -178,7 +178,7 @@ constexpr int kSpinLimit = 1 << 15;  // polls (each with a short sleep) before a
 // then one claim bit per output slice (at most 256 slices).
 constexpr int kCtlStride = 64;
 constexpr int kCtlStarted = 0, kCtlFinished = 1, kCtlExited = 2, kCtlClaim = 8;
-constexpr int kFastSplits = 16;  // split counts whose partials one thread requests at once
+constexpr int kFastSplits = kFastMergeSplits;  // split counts whose partials one thread requests at once
 
 // Merges the split partials of output quads [q0, q0 + count) of one (sequence, KV head)
 // (quad q = packed row q / 32, dims 4(q % 32) .. +3): out = v_scale * sum_s w_s O_s / sum_s
