@@ -371,7 +371,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   }
   if (s >= nsplit) return;
   // in-kernel split merge: count the resident work groups of the pair
-  uint32_t* const ctl = a.ws_ctl + kCtlStride * (int64_t)bg;  // started, finished, claimed, exited
+  uint32_t* const ctl = a.ws_ctl + kCtlStride * (int64_t)bg;  // counters and claim bits of the pair
   const bool fused = a.fused_combine && nsplit > 1;
   const int group_wgs = nsplit * RG;  // work groups that write partials of this pair
   if (fused && threadIdx.x == 0)
