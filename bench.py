@@ -216,8 +216,8 @@ def run_suite(iters):
     stream = torch.cuda.Stream()
     out = {}
 
-    def layer_step(lay, fused=True):
-        gl = PagedLayer(lay)
+    def layer_step(lay, fused=True, layout=0):
+        gl = PagedLayer(lay, layout=layout)
         gl.prefill()
         gl.stage_step()
         if fused:
@@ -304,6 +304,14 @@ def run_suite(iters):
             out[f"c5_m{q_len}_{'fp8' if fp8 else 'bf16'}"] = rec
             del gl
             torch.cuda.empty_cache()
+            if fp8:
+                # the FP8 cache through the BF16 cache's kernel (layout 3): the same-kernel comparison
+                gl = layer_step(lay, fused=False, layout=3)
+                dm, _ = _time_calls(lambda: gl.decode(stream), stream, max(20, iters // 4), 5)
+                out[f"c5_m{q_len}_fp8_layout3"] = {"decode_us": round(dm * 1e3, 2), "kv_bytes": kv,
+                                                   "decode_kv_gbs": round(kv / (dm * 1e-3) / 1e9, 1)}
+                del gl
+                torch.cuda.empty_cache()
     return out
 
 

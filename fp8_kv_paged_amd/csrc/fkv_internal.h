@@ -36,6 +36,8 @@ struct DecodePlan {
   size_t ws_o_bytes;   // fp32 partial outputs
   size_t ws_ml_bytes;  // fp32 (m, l) per partial row
   size_t ws_ctl_bytes; // in-kernel split merge: 256 bytes of counters and claim bits per pair
+  size_t ws_ctl_offset; // where those counters start (after every partial region the layout
+                        // choice of the descriptor may use)
   int fused_combine;   // layout 5 with the whole grid resident: splits merged inside the kernel
   int key_lanes;       // 32-row kernel: key lanes per work group
   int align_splits;    // 32-row kernel, row-exact mode: split boundaries at absolute tile indices

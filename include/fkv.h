@@ -140,6 +140,8 @@ typedef struct fkv_decode_desc {
   int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
                                   (at most 128 with layouts 0, 1, 3, 4, 5 and 6)            */
   int32_t layout;              /* work-group layout: 0 = automatic (layout 5 for an FP8 cache,
+                                  except layout 3 for fkv_decode_attn when the packed rows
+                                  of a KV head fit one 16-row tile and row_exact is 0;
                                   layout 3 for a BF16 cache); 1 = query rows spread over
                                   row groups of at most 32 rows per wave (two waves per SIMD);
                                   2 = all query rows of a KV head in every wave (one per SIMD);
@@ -176,7 +178,9 @@ typedef struct fkv_decode_desc {
 /*
  * Bytes of device workspace fkv_decode_attn needs for (cache, desc): split-KV
  * partial results and, for layout 5, 256 bytes of merge counters per (sequence,
- * KV head) at its end. Pure host arithmetic; may be 0. The workspace must be
+ * KV head) at its end. With the automatic layout and one 16-row tile of an FP8
+ * cache the size covers both kernels that fkv_decode_attn and fkv_insert_decode
+ * then run, so one workspace serves both calls. Pure host arithmetic; may be 0. The workspace must be
  * zero-filled once before its first use (the counters must start at zero); every
  * call returns the counters to zero, so it can then be reused without clearing.
  * One call at a time may use a workspace. Errors as fkv_decode_attn's validation.

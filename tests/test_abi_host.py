@@ -190,6 +190,26 @@ def test_row_exact_plan_rules():
     assert sw - ctl == (_ws(c, row_groups=2, split_tiles=4, window_left=511, **kw) - ctl) * 6 // 5
 
 
+def test_automatic_q1_workspace_covers_both_kernels():
+    """Automatic layout, FP8, one 16-row tile (q1 at 9 heads per KV head): fkv_decode_attn runs the
+    row-group kernel and fkv_insert_decode the 32-row kernel on the same workspace, so its size is
+    the larger partial region of the two plus the 32-row kernel's merge counters."""
+    c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
+    for ctx, nseq in ((8192, 1), (32768, 1), (2048, 4)):
+        kw = dict(num_seqs=nseq, num_q_heads=72, max_blocks_per_seq=(ctx + 63) // 64, max_seq_len=ctx, q_len=1)
+        ctl = (nseq * 8 * 256 + 255) // 256 * 256
+        rows = _ws(c, layout=3, **kw)
+        m32 = _ws(c, layout=5, **kw)
+        assert _ws(c, **kw) == max(rows, m32 - ctl) + ctl, (ctx, nseq)
+    # more rows, row-exact mode and BF16 caches keep their single plan
+    kw = dict(num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192)
+    assert _ws(c, q_len=2, **kw) == _ws(c, q_len=2, layout=5, **kw)
+    assert _ws(c, q_len=1, row_exact=1, split_tiles=16, **kw) == _ws(c, q_len=1, layout=5, row_exact=1,
+                                                                     split_tiles=16, **kw)
+    c16 = _fake_cache(num_blocks=4096, bs=64, hkv=8, dt="bf16")
+    assert _ws(c16, q_len=1, **kw) == _ws(c16, q_len=1, layout=3, **kw)
+
+
 def test_insert_decode_fails_closed_without_touching_the_gpu():
     L = fkv.lib()
     c = _fake_cache()

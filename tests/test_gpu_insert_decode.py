@@ -53,7 +53,12 @@ def _fused_vs_separate(lay, label, **kw):
     fused = PagedLayer(lay, **kw)
     fused.prefill()
     fused.stage_new_tokens()
-    sep = PagedLayer(lay, **kw).build()
+    # the fused call runs the 32-row kernel; with the automatic layout a separate q1 decode
+    # would run the row-group kernel, so the separate reference names layout 5
+    sep_kw = dict(kw)
+    if sep_kw.get("layout", 0) == 0:
+        sep_kw["layout"] = 5
+    sep = PagedLayer(lay, **sep_kw).build()
     before = fkv.get_counters()["insert_decode_launches"]
     out_f = fused.insert_decode().clone()
     out_s = sep.decode().clone()
@@ -113,6 +118,25 @@ def test_sliding_windows(window_left):
 def test_row_exact_mode():
     lay = synth.tiny_layer(419, [3000, 257, 12, 5], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=12)
     _fused_vs_separate(lay, "row exact", split_tiles=8, row_exact=1)
+
+
+def test_q1_decode_and_fused_share_one_workspace():
+    """Automatic layout, one query row per sequence: fkv_decode_attn runs the row-group kernel,
+    fkv_insert_decode the 32-row kernel with its in-kernel merge counters. Alternating calls on
+    one workspace stay correct and leave the counters zero."""
+    lay = synth.tiny_layer(421, [3000, 257], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=1)
+    gl = PagedLayer(lay)
+    gl.prefill()
+    gl.stage_new_tokens()
+    nws = fkv.decode_workspace_bytes(gl.cache, gl.ddesc)
+    ctl = lay.num_seqs * lay.num_kv_heads * 256
+    for rep in range(3):
+        out_f = gl.insert_decode().clone()
+        out_d = gl.decode().clone()
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(gl.workspace[nws - ctl:nws]).item() == 0, rep
+        _check(lay, out_f, f"q1 fused {rep}")
+        _check(lay, out_d, f"q1 decode {rep}")
 
 
 def test_single_query():
