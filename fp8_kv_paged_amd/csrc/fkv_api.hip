@@ -76,7 +76,9 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
   if (d->q_len > FKV_MAX_Q_LEN) return FKV_EUNSUPPORTED;
-  if (d->out_dtype != FKV_OUT_F32) return FKV_EUNSUPPORTED;
+  if (d->out_dtype != FKV_OUT_F32 && d->out_dtype != FKV_OUT_BF16) return FKV_EUNSUPPORTED;
+  // BF16 output: the row-group and 32-row kernels and their merges (layouts 1, 2 and 4 write fp32 only)
+  if (d->out_dtype == FKV_OUT_BF16 && (layout == 1 || layout == 2 || layout == 4)) return FKV_EUNSUPPORTED;
   if (d->num_seqs > 65535) return FKV_EUNSUPPORTED;
   const int64_t group = d->num_q_heads / hkv;
   const int64_t rows = group * d->q_len;
@@ -319,6 +321,7 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.out = static_cast<float*>(out);
+  a.out_bf16 = desc->out_dtype == FKV_OUT_BF16 ? 1 : 0;
   a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
   a.ws_ctl = p.ws_ctl_bytes ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_ctl_offset) : nullptr;

@@ -892,7 +892,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int k
   const float vsc = kfp8 ? *a.v_scale : 1.0f;
   const float mul = lrun > 0.f ? vsc / lrun : 0.f;
   const int i = r / G, h = g * G + (r - i * G);
-  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4) = acc * mul;
+  store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4, acc * mul);
 }
 
 template <int NTW, int R, int K, bool kFp8>

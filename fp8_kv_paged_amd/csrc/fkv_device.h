@@ -14,6 +14,20 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// Stores output elements e .. e+3 of a [seq][M][Hq][128] result: fp32, or BF16 rounded to
+// nearest even (the branch is uniform: one output type per call).
+__device__ __forceinline__ void store_out4(float* out, bool bf16, int64_t e, f32x4_t v) {
+  if (bf16) {
+    const bf16x2_t lo = __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t);
+    const bf16x2_t hi = __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t);
+    *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(out) + e) =
+        u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  } else {
+    *reinterpret_cast<f32x4_t*>(out + e) = v;
+  }
+}
 
 constexpr int kHeadDim = 128;
 constexpr int kTile = 32;     // keys per attention tile

@@ -66,6 +66,7 @@ struct DecodeArgs {
   int32_t fused_combine;  // 32-row kernel: merge the splits inside the kernel (no combine launch)
   int32_t key_lanes;      // 32-row kernel: key lanes per work group
   int32_t align_splits;   // 32-row kernel: splits start at multiples of tiles_per_split (row-exact mode)
+  int32_t out_bf16;       // out holds BF16 (rounded to nearest even), else fp32
   float softmax_scale;
 };
 

@@ -239,8 +239,8 @@ __device__ __forceinline__ void merge_slice(const DecodeArgs& a, int b, int g, i
         if (s0 + j < nsplit) acc += os[j] * wr[s0 + j];
     }
     const int i = r / G, hq = g * G + (r - i * G);
-    *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) =
-        acc * mul[r - r0];
+    store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4,
+        acc * mul[r - r0]);
   }
   __syncthreads();  // the LDS weights are free again
 }
@@ -290,7 +290,8 @@ __device__ __forceinline__ void quad_finish(const DecodeArgs& a, int b, int g, i
   for (int j = 0; j < kFastSplits; ++j)
     if (j < nsplit) acc += x.o[j] * w[j];
   const int G = a.group, i = r / G, hq = g * G + (r - i * G);
-  *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * a.q_len + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) = acc * mul;
+  store_out4(a.out, a.out_bf16, (((int64_t)b * a.q_len + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4,
+      acc * mul);
 }
 
 }  // namespace
@@ -363,8 +364,8 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       for (int idx = threadIdx.x; idx < GM * (kHeadDim / 4); idx += S::kThreads) {
         const int r = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
         const int i = r / G, hq = g * G + (r - i * G);
-        *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) =
-            f32x4_t{0.f, 0.f, 0.f, 0.f};
+        store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4,
+            f32x4_t{0.f, 0.f, 0.f, 0.f});
       }
     }
     return;
@@ -888,8 +889,8 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       const int i = (row0 + rr) / G, hq = g * G + (row0 + rr - i * G);
       const float lw = sm_row[kRows + rr];
       const float mul = lw > 0.f ? vsc / lw : 0.f;
-      *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4) =
-          *reinterpret_cast<const f32x4_t*>(stage + rr * kStageStride + 4 * d4) * mul;
+      store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4,
+          *reinterpret_cast<const f32x4_t*>(stage + rr * kStageStride + 4 * d4) * mul);
     }
   } else {
     // the partial: rows_pad x 128 fp32 (only the GM real rows written), then (M, L) per row

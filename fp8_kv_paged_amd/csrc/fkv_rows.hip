@@ -121,8 +121,8 @@ void decode_rows_kernel(DecodeArgs a) {
         const int r = R0 + idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
         if (r >= GM) continue;
         const int i = r / G, h = g * G + (r - i * G);
-        *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4) =
-            f32x4_t{0.f, 0.f, 0.f, 0.f};
+        store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4,
+            f32x4_t{0.f, 0.f, 0.f, 0.f});
       }
     }
     return;
@@ -448,7 +448,8 @@ void decode_rows_kernel(DecodeArgs a) {
     if (direct) {
       const int i = r / G, h = g * G + (r - i * G);
       const float mul = lw > 0.f ? vsc / lw : 0.f;
-      *reinterpret_cast<f32x4_t*>(a.out + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4) = val * mul;
+      store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 4 * d4,
+          val * mul);
     } else {
       *reinterpret_cast<f32x4_t*>(a.ws_o + (part * a.rows_pad + r) * kHeadDim + 4 * d4) = val;
       if (d4 == 0) {

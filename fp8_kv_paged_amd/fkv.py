@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libfkv.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 FP8_E4M3FN, BF16 = 1, 2
 OUT_F32 = 1
+OUT_BF16 = 2
 HEAD_DIM = 128
 CACHE_DTYPES = {"fp8_e4m3fn": FP8_E4M3FN, "bf16": BF16}
 
@@ -146,10 +147,15 @@ def insert(cache, k, v, slot_mapping, k_scale, v_scale, stream=None):
 
 
 def make_decode_desc(num_seqs, q_len, num_q_heads, max_blocks_per_seq, max_seq_len, window_left=-1,
-                     softmax_scale=1.0 / math.sqrt(HEAD_DIM), split_tiles=0, layout=0, row_groups=0, row_exact=0):
+                     softmax_scale=1.0 / math.sqrt(HEAD_DIM), split_tiles=0, layout=0, row_groups=0, row_exact=0,
+                     out_dtype=OUT_F32):
     return DecodeDesc(int(num_seqs), int(q_len), int(num_q_heads), int(max_blocks_per_seq), int(max_seq_len),
-                      int(window_left), float(softmax_scale), OUT_F32, int(split_tiles), int(layout), int(row_groups),
-                      int(row_exact))
+                      int(window_left), float(softmax_scale), int(out_dtype), int(split_tiles), int(layout),
+                      int(row_groups), int(row_exact))
+
+
+def _out_size(desc):
+    return 2 if desc.out_dtype == OUT_BF16 else 4
 
 
 def decode_workspace_bytes(cache, desc):
@@ -160,7 +166,8 @@ def decode_workspace_bytes(cache, desc):
 
 
 def decode_attn(cache, desc, q, block_table, seq_lens, k_scale, v_scale, out, workspace=None, stream=None):
-    """q BF16 [B, M, Hq, 128]; block_table int32 [B, max_blocks]; seq_lens int32 [B]; out fp32 [B, M, Hq, 128]."""
+    """q BF16 [B, M, Hq, 128]; block_table int32 [B, max_blocks]; seq_lens int32 [B]; out fp32 [B, M, Hq, 128]
+    (BF16 when desc.out_dtype is OUT_BF16)."""
     B, M, Hq = desc.num_seqs, desc.q_len, desc.num_q_heads
     if q.numel() != B * M * Hq * HEAD_DIM or out.numel() != B * M * Hq * HEAD_DIM:
         raise ValueError("q / out do not match the decode descriptor")
@@ -170,7 +177,7 @@ def decode_attn(cache, desc, q, block_table, seq_lens, k_scale, v_scale, out, wo
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().fkv_decode_attn(ctypes.byref(cache), ctypes.byref(desc), _ptr(q, "q", 2),
                                  _ptr(block_table, "block_table", 4), _ptr(seq_lens, "seq_lens", 4),
-                                 _ptr(k_scale, "k_scale", 4), _ptr(v_scale, "v_scale", 4), _ptr(out, "out", 4), ws,
+                                 _ptr(k_scale, "k_scale", 4), _ptr(v_scale, "v_scale", 4), _ptr(out, "out", _out_size(desc)), ws,
                                  ws_bytes, _stream(stream)),
            "fkv_decode_attn")
 
@@ -192,7 +199,7 @@ def insert_decode(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, 
     _check(lib().fkv_insert_decode(ctypes.byref(cache), ctypes.byref(desc), _ptr(q, "q", 2), _ptr(k_new, "k_new", 2),
                                    _ptr(v_new, "v_new", 2), _ptr(block_table, "block_table", 4),
                                    _ptr(seq_lens, "seq_lens", 4), _ptr(k_scale, "k_scale", 4),
-                                   _ptr(v_scale, "v_scale", 4), _ptr(out, "out", 4), ws, ws_bytes, _stream(stream)),
+                                   _ptr(v_scale, "v_scale", 4), _ptr(out, "out", _out_size(desc)), ws, ws_bytes, _stream(stream)),
            "fkv_insert_decode")
 
 

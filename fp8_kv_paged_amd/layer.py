@@ -22,7 +22,8 @@ def to_dev_bits(bits, device):
 
 
 class PagedLayer:
-    def __init__(self, lay, device="cuda", poison=True, split_tiles=0, layout=0, row_groups=0, row_exact=0):
+    def __init__(self, lay, device="cuda", poison=True, split_tiles=0, layout=0, row_groups=0, row_exact=0,
+                 out_bf16=False):
         self.lay = lay
         self.device = device
         self.desc = fkv.make_cache_desc(lay.num_blocks, lay.block_size, lay.num_kv_heads, lay.cache_dtype)
@@ -38,10 +39,10 @@ class PagedLayer:
         self.max_seq_len = int(max(1, lay.seq_lens.max())) if lay.num_seqs else 1
         self.ddesc = fkv.make_decode_desc(lay.num_seqs, lay.q_len, lay.num_q_heads, lay.max_blocks, self.max_seq_len,
                                           lay.window_left, lay.softmax_scale, split_tiles, layout, row_groups,
-                                          row_exact)
+                                          row_exact, fkv.OUT_BF16 if out_bf16 else fkv.OUT_F32)
         self.q = to_dev_bits(lay.q_bits(), device)
-        self.out = torch.empty((lay.num_seqs, lay.q_len, lay.num_q_heads, HEAD_DIM), dtype=torch.float32,
-                               device=device)
+        self.out = torch.empty((lay.num_seqs, lay.q_len, lay.num_q_heads, HEAD_DIM),
+                               dtype=torch.bfloat16 if out_bf16 else torch.float32, device=device)
         nws = fkv.decode_workspace_bytes(self.cache, self.ddesc)
         # zero once: the split-merge counters at its end must start at zero (calls leave them so)
         self.workspace = torch.zeros((max(nws, 16),), dtype=torch.uint8, device=device)

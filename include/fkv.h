@@ -45,6 +45,7 @@ extern "C" {
 
 /* ---- output types ------------------------------------------------------------------------ */
 #define FKV_OUT_F32 1
+#define FKV_OUT_BF16 2
 
 #define FKV_HEAD_DIM 128
 #define FKV_MAX_Q_LEN 16
@@ -136,7 +137,10 @@ typedef struct fkv_decode_desc {
   int32_t max_seq_len;         /* host upper bound on seq_lens[], sizes the split grid      */
   int32_t window_left;         /* -1 = global; w >= 0: keys p-w..p visible to position p    */
   float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
-  int32_t out_dtype;           /* FKV_OUT_F32                                               */
+  int32_t out_dtype;           /* FKV_OUT_F32 (out is float) or FKV_OUT_BF16 (out is BF16,
+                                  each fp32 result rounded to nearest even; the activations
+                                  of the models are BF16: [P1] Contract). BF16 with layouts
+                                  0, 3, 5 and 6 only, else FKV_EUNSUPPORTED               */
   int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
                                   (at most 128 with layouts 0, 1, 3, 4, 5 and 6)            */
   int32_t layout;              /* work-group layout: 0 = automatic (layout 5 for an FP8 cache,
@@ -196,7 +200,8 @@ int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* de
  *               INCLUDING the q_len new tokens (already inserted on this stream);
  *               q_len <= L <= min(max_seq_len, max_blocks_per_seq*block_size)
  *  k_scale, v_scale  device fp32 scalars (FP8 cache; ignored for BF16)
- *  out          device fp32 [num_seqs][q_len][num_q_heads][128]
+ *  out          device fp32 (out_dtype FKV_OUT_F32) or BF16 (FKV_OUT_BF16)
+ *               [num_seqs][q_len][num_q_heads][128], 16-byte aligned
  *
  * Query row i sits at position p = L - q_len + i. Key j is visible to it iff
  * lo <= j <= p with lo = 0 (window_left = -1) or max(0, p - window_left). Query

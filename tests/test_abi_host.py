@@ -210,6 +210,24 @@ def test_automatic_q1_workspace_covers_both_kernels():
     assert _ws(c16, q_len=1, **kw) == _ws(c16, q_len=1, layout=3, **kw)
 
 
+def test_bf16_output_plan_rules():
+    """BF16 output: the row-group and 32-row kernels (layouts 0, 3, 5, 6) write it with the same
+    plan and workspace as fp32; layouts 1, 2 and 4 and unknown output types fail closed."""
+    c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
+    kw = dict(num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192)
+    for layout in (0, 3, 5, 6):
+        for q_len in (1, 12):
+            if layout == 6 and q_len == 1:
+                continue
+            assert (_ws(c, layout=layout, q_len=q_len, out_dtype=fkv.OUT_BF16, **kw)
+                    == _ws(c, layout=layout, q_len=q_len, **kw)), (layout, q_len)
+    for bad in (dict(layout=1, out_dtype=fkv.OUT_BF16), dict(layout=2, out_dtype=fkv.OUT_BF16),
+                dict(layout=4, out_dtype=fkv.OUT_BF16), dict(out_dtype=0), dict(out_dtype=3)):
+        with pytest.raises(fkv.FkvError) as e:
+            _ws(c, **kw, **bad)
+        assert e.value.status == fkv.EUNSUPPORTED, bad
+
+
 def test_insert_decode_fails_closed_without_touching_the_gpu():
     L = fkv.lib()
     c = _fake_cache()
