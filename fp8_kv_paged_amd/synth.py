@@ -206,3 +206,66 @@ def tiny_layer(seed, seq_lens, num_q_heads=18, num_kv_heads=2, block_size=32, q_
     return make_layer(f"tiny{seed}", seed, 0, num_q_heads, num_kv_heads, block_size, q_len, window_left, seq_lens,
                       cache_dtype=cache_dtype, pool_slack=pool_slack, outlier_rate=outlier_rate,
                       fixed_scale=fixed_scale)
+
+
+# ---- inputs of the Q/K RMSNorm + RoPE + insert step -------------------------------------
+
+ROPE_BASE = 1.0e6  # rotary base of the synthetic table (the method takes the table as given)
+
+
+def rope_table(num_positions, base=ROPE_BASE):
+    """float32 [P, 128]: row p holds cos(p * f_i) for i < 64, then sin(p * f_i), with
+    f_i = base^(-i / 64); computed in float64, then rounded to float32."""
+    p = np.arange(num_positions, dtype=np.float64)[:, None]
+    f = base ** (-np.arange(HEAD_DIM // 2, dtype=np.float64) / (HEAD_DIM // 2))
+    ang = p * f[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+@dataclass
+class NormRopeStep:
+    """T new tokens before the norm/RoPE/insert step: raw BF16 Q, K, V, the norm weights,
+    positions and slots (into a layer's pool) and the scales."""
+    q_bits: np.ndarray          # uint16 [T, Hq, 128]
+    k_bits: np.ndarray          # uint16 [T, Hkv, 128]
+    v_bits: np.ndarray          # uint16 [T, Hkv, 128]
+    q_w: np.ndarray             # uint16 [128]
+    k_w: np.ndarray             # uint16 [128]
+    eps: float
+    cos_sin: np.ndarray         # float32 [P, 128]
+    positions: np.ndarray       # int32 [T]
+    slot_mapping: np.ndarray    # int32 [T]
+
+
+def norm_rope_step(lay, seed=77, eps=1e-6, table_rows=None):
+    """The M new tokens of every sequence of `lay` (positions L - M .. L - 1, slots through
+    its block table) with raw Q/K/V ~ N(0, 1) (K, V with the layer's outlier channels, Q
+    scaled by 4 so the norm does real work) and norm weights ~ U(0.5, 1.5), BF16."""
+    r = _rng(seed, lay.seed, lay.layer_id)
+    M, B = lay.q_len, lay.num_seqs
+    T = M * B
+    q = r.standard_normal((T, lay.num_q_heads, HEAD_DIM), dtype=np.float32) * np.float32(4.0)
+    ks, vs, pos, slots = [], [], [], []
+    for b in range(B):
+        L = int(lay.seq_lens[b])
+        t0 = L - M
+        kb, vb = lay.kv_bits(b, max(t0, 0), L)
+        pad = max(0, -t0)
+        if pad:  # rows before position 0: padding tokens (any values, never inserted)
+            kb = np.concatenate([np.zeros((pad,) + kb.shape[1:], np.uint16), kb])
+            vb = np.concatenate([np.zeros((pad,) + vb.shape[1:], np.uint16), vb])
+        ks.append(kb)
+        vs.append(vb)
+        p = np.arange(t0, L)
+        pos.append(p)
+        sl = np.full(M, -1, dtype=np.int64)
+        ok = p >= 0
+        sl[ok] = lay.slots(b, max(t0, 0), L)
+        slots.append(sl)
+    positions = np.concatenate(pos).astype(np.int32)
+    P = table_rows if table_rows is not None else int(max(1, positions.max() + 1))
+    w = r.uniform(0.5, 1.5, size=(2, HEAD_DIM)).astype(np.float32)
+    return NormRopeStep(q_bits=f32_to_bf16_bits(q), k_bits=np.concatenate(ks), v_bits=np.concatenate(vs),
+                        q_w=f32_to_bf16_bits(w[0]), k_w=f32_to_bf16_bits(w[1]), eps=float(eps),
+                        cos_sin=rope_table(P), positions=positions,
+                        slot_mapping=np.concatenate(slots).astype(np.int32))

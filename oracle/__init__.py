@@ -17,10 +17,11 @@ Modules:
   e4m3       -- E4M3FN decode/encode and the scaled quantiser
   paged      -- cache sizes, the pool byte layout, insertion and gather
   attention  -- dense decode attention over the dequantised cache
+  normrope   -- per-head Q/K RMSNorm and RoPE ahead of the scaled insert
 
 Every function here is pinned by a test under tests/ against something other
 than itself (library routine, printed payload figures, closed forms,
 invariants, brute force); none is "parity unpinned".
 """
 
-from . import e4m3, paged, attention  # noqa: F401
+from . import e4m3, paged, attention, normrope  # noqa: F401
