@@ -224,6 +224,21 @@ def run_suite(iters):
             gl.stage_new_tokens()
         return gl
 
+    # Q/K RMSNorm + RoPE + insert of one step's new tokens (72/8 heads): the 8k layer's 12
+    # tokens and the 32-sequence batch's 384. Bytes: raw Q, K, V and the table rows read,
+    # rotated Q and the FP8 K/V written.
+    for name, lay in (("norm_rope_insert_c3_m12", synth.c3_layer(8192, 64)),
+                      ("norm_rope_insert_c5_m12", synth.c5_layer(q_len=12))):
+        gl = PagedLayer(lay)
+        gl.stage_norm_rope(synth.norm_rope_step(lay))
+        nm, _ = _time_calls(lambda: gl.norm_rope_insert(stream), stream, iters, 20)
+        T = lay.num_seqs * lay.q_len
+        nbytes = T * (lay.num_q_heads * 128 * 2 * 2 + lay.num_kv_heads * 128 * (2 + 2 + 1 + 1) + 128 * 4 + 8)
+        out[name] = {"us": round(nm * 1e3, 3), "tokens": T, "bytes": nbytes,
+                     "gbs": round(nbytes / (nm * 1e-3) / 1e9, 1)}
+        del gl
+        torch.cuda.empty_cache()
+
     for name, make in (("c1", synth.c1_layer), ("c2", synth.c2_layer)):
         lay = make()
         gl = layer_step(lay)

@@ -19,6 +19,7 @@ std::atomic<uint64_t> g_insert[2];
 std::atomic<uint64_t> g_split[2][9];
 std::atomic<uint64_t> g_combine;
 std::atomic<uint64_t> g_insert_decode;
+std::atomic<uint64_t> g_norm_rope[2];
 std::atomic<uint64_t> g_rejected;
 
 int reject(int code) {
@@ -282,6 +283,49 @@ int fkv_insert(const fkv_cache* cache, const uint16_t* k, const uint16_t* v, con
   return FKV_OK;
 }
 
+int fkv_qk_norm_rope_insert(const fkv_cache* cache, int32_t num_tokens, int32_t num_q_heads, const uint16_t* q,
+                            const uint16_t* k, const uint16_t* v, const uint16_t* q_weight, const uint16_t* k_weight,
+                            float eps, const float* cos_sin, int32_t rope_rows, const int32_t* positions,
+                            const int32_t* slot_mapping, const float* k_scale, const float* v_scale, uint16_t* q_out,
+                            void* stream) {
+  int rc = check_cache(cache);
+  if (rc) return reject(rc);
+  if (num_tokens < 0 || num_q_heads < 1 || num_q_heads % cache->desc.num_kv_heads != 0 || rope_rows < 1)
+    return reject(FKV_EINVAL);
+  if (!(std::isfinite(eps) && eps >= 0.f)) return reject(FKV_EINVAL);
+  if (num_tokens == 0) return FKV_OK;
+  const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
+  const void* p16[] = {q, k, v, q_weight, k_weight, cos_sin, q_out};
+  for (const void* ptr : p16)
+    if (!ptr || !aligned(ptr, 16)) return reject(FKV_EINVAL);
+  if (!positions || !slot_mapping || !aligned(positions, 4) || !aligned(slot_mapping, 4)) return reject(FKV_EINVAL);
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))) return reject(FKV_EINVAL);
+  fkv::NormRopeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q_w = q_weight;
+  a.k_w = k_weight;
+  a.cos_sin = cos_sin;
+  a.positions = positions;
+  a.slots = slot_mapping;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.q_out = q_out;
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->desc.num_kv_heads;
+  a.block_size = cache->desc.block_size;
+  a.rope_rows = rope_rows;
+  a.num_slots = (int64_t)cache->desc.num_blocks * cache->desc.block_size;
+  a.eps = eps;
+  if (fkv::launch_norm_rope_insert(a, fp8, static_cast<hipStream_t>(stream)) != hipSuccess) return reject(FKV_EHIP);
+  g_norm_rope[fp8 ? 0 : 1].fetch_add(1, std::memory_order_relaxed);
+  return FKV_OK;
+}
+
 int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* desc, size_t* bytes) {
   if (!bytes) return reject(FKV_EINVAL);
   fkv::DecodePlan p;
@@ -392,6 +436,7 @@ int fkv_get_counters(fkv_counters* out) {
   out->decode_combine_launches = g_combine.load(std::memory_order_relaxed);
   out->insert_decode_launches = g_insert_decode.load(std::memory_order_relaxed);
   out->rejected_calls = g_rejected.load(std::memory_order_relaxed);
+  for (int i = 0; i < 2; ++i) out->norm_rope_insert_launches[i] = g_norm_rope[i].load(std::memory_order_relaxed);
   return FKV_OK;
 }
 
@@ -402,6 +447,8 @@ int fkv_reset_counters(void) {
   }
   g_combine.store(0);
   g_insert_decode.store(0);
+  g_norm_rope[0].store(0);
+  g_norm_rope[1].store(0);
   g_rejected.store(0);
   return FKV_OK;
 }

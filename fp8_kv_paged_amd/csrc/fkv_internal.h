@@ -71,6 +71,26 @@ struct DecodeArgs {
 };
 
 hipError_t launch_insert(const InsertArgs& a, bool fp8, hipStream_t stream);
+
+struct NormRopeArgs {
+  const uint16_t* q;        // BF16 [T][Hq][128]
+  const uint16_t* k;        // BF16 [T][Hkv][128]
+  const uint16_t* v;        // BF16 [T][Hkv][128]
+  const uint16_t* q_w;      // BF16 [128]
+  const uint16_t* k_w;      // BF16 [128]
+  const float* cos_sin;     // fp32 [rope_rows][128]: 64 cosines, then 64 sines
+  const int32_t* positions; // [T]
+  const int32_t* slots;     // [T]
+  const float* k_scale;
+  const float* v_scale;
+  uint16_t* q_out;          // BF16 [T][Hq][128] (may be q itself)
+  void* k_pool;
+  void* v_pool;
+  int32_t num_tokens, num_q_heads, num_kv_heads, block_size, rope_rows;
+  int64_t num_slots;
+  float eps;
+};
+hipError_t launch_norm_rope_insert(const NormRopeArgs& a, bool fp8, hipStream_t stream);
 // Work-group shape of the split kernel: R row groups of NTW row tiles each, K key lanes
 // per group (R*K waves), and how many such groups one CU holds at once.
 struct SplitShapeInfo {

@@ -50,7 +50,7 @@ class DecodeDesc(ctypes.Structure):
 class Counters(ctypes.Structure):
     _fields_ = [("insert_launches", ctypes.c_uint64 * 2), ("decode_split", (ctypes.c_uint64 * 9) * 2),
                 ("decode_combine_launches", ctypes.c_uint64), ("rejected_calls", ctypes.c_uint64),
-                ("insert_decode_launches", ctypes.c_uint64)]
+                ("insert_decode_launches", ctypes.c_uint64), ("norm_rope_insert_launches", ctypes.c_uint64 * 2)]
 
 
 _lib = None
@@ -72,12 +72,14 @@ def lib():
                                       sz, vp]
         L.fkv_insert_decode.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, sz, vp]
+        L.fkv_qk_norm_rope_insert.argtypes = [ctypes.POINTER(Cache), i32, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp,
+                                              i32, vp, vp, vp, vp, vp, vp]
         L.fkv_status_string.argtypes = [ctypes.c_int]
         L.fkv_status_string.restype = ctypes.c_char_p
         L.fkv_get_counters.argtypes = [ctypes.POINTER(Counters)]
         L.fkv_reset_counters.argtypes = []
         for f in ("fkv_cache_bytes", "fkv_init_cache", "fkv_insert", "fkv_decode_workspace_bytes", "fkv_decode_attn",
-                  "fkv_insert_decode", "fkv_get_counters", "fkv_reset_counters"):
+                  "fkv_insert_decode", "fkv_qk_norm_rope_insert", "fkv_get_counters", "fkv_reset_counters"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,6 +205,31 @@ def insert_decode(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, 
            "fkv_insert_decode")
 
 
+def qk_norm_rope_insert(cache, q, k, v, q_weight, k_weight, eps, cos_sin, positions, slot_mapping, k_scale, v_scale,
+                        q_out, stream=None):
+    """fkv_qk_norm_rope_insert: q BF16 [T, Hq, 128], k / v BF16 [T, Hkv, 128], weights BF16 [128],
+    cos_sin fp32 [P, 128], positions / slot_mapping int32 [T], q_out BF16 like q (may be q)."""
+    T = int(positions.numel())
+    Hkv = cache.desc.num_kv_heads
+    if q.dim() != 3 or q.shape[0] != T or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [num_tokens, num_q_heads, 128]")
+    Hq = int(q.shape[1])
+    for name, t, n in (("k", k, T * Hkv * HEAD_DIM), ("v", v, T * Hkv * HEAD_DIM), ("q_out", q_out, q.numel()),
+                       ("q_weight", q_weight, HEAD_DIM), ("k_weight", k_weight, HEAD_DIM),
+                       ("slot_mapping", slot_mapping, T)):
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
+        raise ValueError("cos_sin must be [rope_rows, 128]")
+    _check(lib().fkv_qk_norm_rope_insert(ctypes.byref(cache), T, Hq, _ptr(q, "q", 2), _ptr(k, "k", 2),
+                                         _ptr(v, "v", 2), _ptr(q_weight, "q_weight", 2),
+                                         _ptr(k_weight, "k_weight", 2), float(eps), _ptr(cos_sin, "cos_sin", 4),
+                                         int(cos_sin.shape[0]), _ptr(positions, "positions", 4),
+                                         _ptr(slot_mapping, "slot_mapping", 4), _ptr(k_scale, "k_scale", 4),
+                                         _ptr(v_scale, "v_scale", 4), _ptr(q_out, "q_out", 2), _stream(stream)),
+           "fkv_qk_norm_rope_insert")
+
+
 def get_counters():
     c = Counters()
     _check(lib().fkv_get_counters(ctypes.byref(c)), "fkv_get_counters")
@@ -210,6 +237,7 @@ def get_counters():
             "decode_split": [list(r) for r in c.decode_split],
             "decode_combine_launches": c.decode_combine_launches,
             "insert_decode_launches": c.insert_decode_launches,
+            "norm_rope_insert_launches": list(c.norm_rope_insert_launches),
             "rejected_calls": c.rejected_calls}
 
 

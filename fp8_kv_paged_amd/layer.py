@@ -105,6 +105,22 @@ class PagedLayer:
                           self.k_scale, self.v_scale, self.out, self.workspace, stream)
         return self.out
 
+    def stage_norm_rope(self, st):
+        """Upload a synth.NormRopeStep (raw Q/K/V of the new tokens, weights, table, positions,
+        slots); q_rot receives the normalised, rotated Q."""
+        d = self.device
+        self.nr = {"q": to_dev_bits(st.q_bits, d), "k": to_dev_bits(st.k_bits, d), "v": to_dev_bits(st.v_bits, d),
+                   "q_w": to_dev_bits(st.q_w, d), "k_w": to_dev_bits(st.k_w, d), "eps": st.eps,
+                   "cos_sin": torch.from_numpy(st.cos_sin).to(d), "positions": torch.from_numpy(st.positions).to(d),
+                   "slots": torch.from_numpy(st.slot_mapping).to(d)}
+        self.q_rot = torch.empty_like(self.nr["q"])
+
+    def norm_rope_insert(self, stream=None):
+        n = self.nr
+        fkv.qk_norm_rope_insert(self.cache, n["q"], n["k"], n["v"], n["q_w"], n["k_w"], n["eps"], n["cos_sin"],
+                                n["positions"], n["slots"], self.k_scale, self.v_scale, self.q_rot, stream)
+        return self.q_rot
+
     def insert_step(self, stream=None):
         fkv.insert(self.cache, self.step_k, self.step_v, self.step_slots, self.k_scale, self.v_scale, stream)
 

@@ -251,6 +251,42 @@ int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const
                       const int32_t* seq_lens, const float* k_scale, const float* v_scale, void* out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Per-head Q/K RMSNorm and rotary position embedding of num_tokens new tokens, with the
+ * normalised, rotated K and the raw V inserted into the cache, in one launch ([P1] "Initial
+ * optimization order": the scaled E4M3 insert at the Q/K norm + RoPE step; [P3] "Result
+ * progression and what actually worked": an exact fused Q/K RMSNorm/RoPE stack).
+ *
+ *  q            device BF16 [num_tokens][num_q_heads][128], raw (num_q_heads a multiple
+ *               of the cache's num_kv_heads)
+ *  k, v         device BF16 [num_tokens][num_kv_heads][128], raw
+ *  q_weight, k_weight  device BF16 [128]: the RMSNorm weights of Q and of K
+ *  eps          RMSNorm epsilon (finite, >= 0)
+ *  cos_sin      device fp32 [rope_rows][128]: row p holds cos(p f_i) for i < 64, then
+ *               sin(p f_i); the caller's frequencies f_i (its rotary base)
+ *  positions    device int32 [num_tokens]: the token's position (a row of cos_sin)
+ *  slot_mapping device int32 [num_tokens]: as fkv_insert
+ *  k_scale, v_scale  as fkv_insert
+ *  q_out        device BF16 [num_tokens][num_q_heads][128]; may be q itself (in place)
+ *  all device buffers 16-byte aligned (positions, slot_mapping and the scales 4-byte)
+ *
+ * For every head vector x of Q and K, in float32 with every product, sum and quotient
+ * rounded on its own (no fused multiply-add): s = the sum of x_d^2, each lane of 8
+ * consecutive dims in dim order and then the 16 partial sums combined pairwise at
+ * distances 1, 2, 4 and 8; r = 1 / sqrt(s / 128 + eps); y_d = bf16(x_d r w_d) (round to
+ * nearest even); z_d = bf16(y_d c_d - y_(d+64) s_d) and z_(d+64) = bf16(y_(d+64) c_d +
+ * y_d s_d) for d < 64, with c, s the row of the token's position. q_out receives z of Q;
+ * z of K is inserted as fkv_insert inserts a key (the same bytes for an FP8 or BF16
+ * cache), V as fkv_insert inserts a value. A token whose position is outside [0,
+ * rope_rows) gets a zero q_out row and inserts nothing; a slot outside the pool skips the
+ * insert only. Errors: FKV_EINVAL (bad pointers, sizes, eps), FKV_EHIP.
+ */
+int fkv_qk_norm_rope_insert(const fkv_cache* cache, int32_t num_tokens, int32_t num_q_heads, const uint16_t* q,
+                            const uint16_t* k, const uint16_t* v, const uint16_t* q_weight, const uint16_t* k_weight,
+                            float eps, const float* cos_sin, int32_t rope_rows, const int32_t* positions,
+                            const int32_t* slot_mapping, const float* k_scale, const float* v_scale, uint16_t* q_out,
+                            void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* fkv_status_string(int status);
 
@@ -268,6 +304,7 @@ typedef struct fkv_counters {
   uint64_t rejected_calls;          /* calls that returned an error            */
   uint64_t insert_decode_launches;  /* fkv_insert_decode calls (also counted in
                                        decode_split)                            */
+  uint64_t norm_rope_insert_launches[2];  /* fkv_qk_norm_rope_insert: [0] FP8, [1] BF16 */
 } fkv_counters;
 
 int fkv_get_counters(fkv_counters* out);

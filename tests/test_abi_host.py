@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = fkv.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -246,6 +246,26 @@ def test_insert_decode_fails_closed_without_touching_the_gpu():
     c16 = _fake_cache(dt="bf16")
     assert call(c16, fkv.make_decode_desc(1, 12, 18, 8, 256), dev, dev) == fkv.EUNSUPPORTED
     assert call(c, fkv.make_decode_desc(0, 12, 18, 8, 256), dev, dev) == fkv.OK  # no sequences: no launch
+
+
+def test_norm_rope_insert_fails_closed_without_touching_the_gpu():
+    L = fkv.lib()
+    c = _fake_cache(hkv=2)
+    dev = ctypes.c_void_p(0x300000)
+
+    def call(T=4, Hq=18, eps=1e-6, rows=64, q=dev, ks=dev, cache=c):
+        return L.fkv_qk_norm_rope_insert(ctypes.byref(cache), T, Hq, q, dev, dev, dev, dev, ctypes.c_float(eps), dev,
+                                         rows, dev, dev, ks, dev, dev, None)
+    assert call(T=-1) == fkv.EINVAL
+    assert call(Hq=0) == fkv.EINVAL
+    assert call(Hq=17) == fkv.EINVAL                      # not a multiple of the KV heads
+    assert call(rows=0) == fkv.EINVAL
+    assert call(eps=-1.0) == fkv.EINVAL
+    assert call(eps=float("nan")) == fkv.EINVAL
+    assert call(q=None) == fkv.EINVAL
+    assert call(q=ctypes.c_void_p(0x300008)) == fkv.EINVAL  # 16-byte alignment
+    assert call(ks=None) == fkv.EINVAL                     # FP8 cache needs the scales
+    assert call(T=0) == fkv.OK                             # nothing to do: no launch
 
 
 def test_counters_record_rejections():
