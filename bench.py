@@ -227,8 +227,11 @@ def run_suite(iters):
     # Q/K RMSNorm + RoPE + insert of one step's new tokens (72/8 heads): the 8k layer's 12
     # tokens and the 32-sequence batch's 384. Bytes: raw Q, K, V and the table rows read,
     # rotated Q and the FP8 K/V written.
-    for name, lay in (("norm_rope_insert_c3_m12", synth.c3_layer(8192, 64)),
-                      ("norm_rope_insert_c5_m12", synth.c5_layer(q_len=12))):
+    def progress(msg):
+        print(f"[suite] {msg}", file=sys.stderr, flush=True)
+
+    for name, lay in (("norm_rope_insert_c3_m12", synth.c3_layer(8192, 64)),):
+        progress(name)
         gl = PagedLayer(lay)
         gl.stage_norm_rope(synth.norm_rope_step(lay))
         nm, _ = _time_calls(lambda: gl.norm_rope_insert(stream), stream, iters, 20)
@@ -239,7 +242,24 @@ def run_suite(iters):
         del gl
         torch.cuda.empty_cache()
 
+    # Chunked prefill on the 32-row kernel: 512 new tokens of a 72/8 layer attending to an
+    # 8k prefix and causally to each other (4,608 packed rows per KV head). Algorithmic work:
+    # 4 flops per (row, visible key, dim) for QK^T and PV.
+    for name, M, L in (("prefill_q512_ctx8192", 512, 8192),):
+        progress(name)
+        lay = synth.tiny_layer(1006, [L], num_q_heads=72, num_kv_heads=8, block_size=64, q_len=M)
+        gl = PagedLayer(lay).build()
+        pm, _ = _time_calls(lambda: gl.decode(stream), stream, max(10, iters // 10), 3)
+        vis = sum(L - M + i + 1 for i in range(M))
+        flops = 4 * 128 * lay.num_q_heads * vis
+        out[name] = {"us": round(pm * 1e3, 2), "q_len": M, "context": L, "flops": flops,
+                     "tflops": round(flops / (pm * 1e-3) / 1e12, 1),
+                     "mfma_bf16_frac": round(flops / (pm * 1e-3) / 2.5e15, 3)}
+        del gl
+        torch.cuda.empty_cache()
+
     for name, make in (("c1", synth.c1_layer), ("c2", synth.c2_layer)):
+        progress(name)
         lay = make()
         gl = layer_step(lay)
         fm, _ = _time_calls(lambda: gl.insert_decode(stream), stream, iters, 20)
@@ -252,6 +272,7 @@ def run_suite(iters):
     # C4: 48 target layers (36 sliding-window, 12 global) + 6 draft layers at context 8192;
     # one cycle = one fused insert + decode call per layer. Two copies of the cycle's layers
     # are alternated so consecutive cycles do not find the K/V in the 256 MB Infinity Cache.
+    progress("c4 cycle")
     layers = [synth.c4_layer(i) for i in range(synth.C4_LAYERS + synth.C4_DRAFT_LAYERS)]
     copies = [[layer_step(lay) for lay in layers] for _ in range(2)]
     kv54 = sum(_visible_kv_bytes(lay, 1) for lay in layers)
@@ -304,6 +325,7 @@ def run_suite(iters):
 
     # C5: 32 sequences, 72/8 heads, contexts log-uniform in [1k, 128k], page 32, one pool
     for q_len in (12, 1):
+        progress(f"c5 q_len {q_len}")
         for dt in ("fp8_e4m3fn", "bf16"):
             lay = synth.c5_layer(q_len=q_len, cache_dtype=dt)
             fp8 = dt == "fp8_e4m3fn"
@@ -311,7 +333,7 @@ def run_suite(iters):
             dm, _ = _time_calls(lambda: gl.decode(stream), stream, max(20, iters // 4), 5)
             kv = _visible_kv_bytes(lay, 1 if fp8 else 2)
             rec = {"decode_us": round(dm * 1e3, 2), "kv_bytes": kv, "decode_kv_gbs": round(kv / (dm * 1e-3) / 1e9, 1),
-                   "layout": "5 (32-row kernel)" if fp8 else "3 (row-group kernel)"}
+                   "layout": ("5 (32-row kernel)" if fp8 and q_len > 1 else "3 (row-group kernel)")}
             if fp8:
                 fm, _ = _time_calls(lambda: gl.insert_decode(stream), stream, max(20, iters // 4), 5)
                 rec["fused_step_us"] = round(fm * 1e3, 2)
@@ -480,7 +502,8 @@ def main():
         line["ab"] = extra
     if args.suite:
         line["suite"] = run_suite(args.steps)
-    if not args.no_cpu_baseline:
+    # the CPU baseline belongs to the headline line; the suite's line omits it
+    if not args.no_cpu_baseline and not args.suite:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -76,7 +76,7 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
-  if (d->q_len > FKV_MAX_Q_LEN) return FKV_EUNSUPPORTED;
+  if (d->q_len > FKV_MAX_PREFILL_Q_LEN) return FKV_EUNSUPPORTED;
   if (d->out_dtype != FKV_OUT_F32 && d->out_dtype != FKV_OUT_BF16) return FKV_EUNSUPPORTED;
   // BF16 output: the row-group and 32-row kernels and their merges (layouts 1, 2 and 4 write fp32 only)
   if (d->out_dtype == FKV_OUT_BF16 && (layout == 1 || layout == 2 || layout == 4)) return FKV_EUNSUPPORTED;
@@ -84,7 +84,11 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   const int64_t group = d->num_q_heads / hkv;
   const int64_t rows = group * d->q_len;
   const int nt = (int)((rows + 15) / 16);
-  if (nt > kMaxNT) return FKV_EUNSUPPORTED;
+  // longer query windows (chunked prefill) run on the 32-row kernel only: 64-row work groups
+  const bool long_rows = nt > kMaxNT || d->q_len > FKV_MAX_Q_LEN;
+  if (long_rows && !(c->desc.cache_dtype == FKV_FP8_E4M3FN && (layout == 0 || layout == 5) && !d->row_exact &&
+                     d->row_groups == 0))
+    return FKV_EUNSUPPORTED;
   if (layout == 4 && nt < 3) return FKV_EUNSUPPORTED;  // the wide kernel needs two row halves
   const bool fp8_cache = c->desc.cache_dtype == FKV_FP8_E4M3FN;
   if ((layout == 5 || layout == 6) && !fp8_cache) return FKV_EUNSUPPORTED;  // the 32-row kernel reads FP8 caches
@@ -109,7 +113,8 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
     // 32-row kernel: the rows_pad = 32 * rt_total packed rows of a KV head are cut into RG
     // row groups of separate work groups (on one XCD, sharing K/V tiles through its L2); the
     // splits fill the chip, each key lane takes whole tiles, a split at most 128 tiles.
-    const int rt_total = sh.r;
+    // long query windows: ceil(rows / 64) work groups of two row tiles and four key lanes
+    const int rt_total = long_rows ? (int)((rows + 63) / 64) * 2 : sh.r;
     p->rows_pad = 32 * rt_total;
     if (d->row_groups != 0 && d->row_groups != 1 && d->row_groups != 2 && d->row_groups != 4) return FKV_EINVAL;
     int rg = d->row_groups;
@@ -120,6 +125,7 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
       // (the second reader hits the XCD's L2); measured on the 72/8-head layer at M = 12,
       // two groups beat one and four at both 8k and 32k context.
       rg = rt_total >= 2 ? 2 : 1;
+      if (long_rows) rg = rt_total / 2;
     }
     if (sh.groups_per_cu == -3) {
       // layout 6: two row tiles per work group (both held by each of its four waves)
@@ -177,6 +183,7 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   // aligned splits (row-exact mode) can straddle one more split boundary inside a window
   const int64_t max_splits = (tiles_max + tps - 1) / tps + (p->align_splits && d->window_left >= 0 ? 1 : 0);
   if (max_splits > fkv::kMaxSplits) return FKV_EUNSUPPORTED;
+  if ((int64_t)std::max(d->num_seqs, 1) * hkv * max_splits * p->row_groups > 0x7FFFFFFF) return FKV_EUNSUPPORTED;
   p->tiles_per_split = (int)tps;
   p->max_splits = (int)max_splits;
   // Row-group kernel: with at least eight (sequence, KV head) pairs, each pair's work groups
@@ -197,7 +204,7 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
     const int64_t pairs = (int64_t)d->num_seqs * hkv;
     const int64_t per_pair = max_splits * p->row_groups;
     const int64_t grid = p->xcd_pairs ? (pairs + 7) / 8 * 8 * per_pair : pairs * per_pair;
-    p->fused_combine = grid <= kNumCUs ? 1 : 0;
+    p->fused_combine = (grid <= kNumCUs && !long_rows) ? 1 : 0;  // long windows: the combine kernel
     p->ws_ctl_bytes = round_up((uint64_t)pairs * 256, kAlign);  // 256 bytes of counters per pair
   }
   p->ws_bytes = p->ws_o_bytes + p->ws_ml_bytes + p->ws_ctl_bytes;
@@ -345,6 +352,7 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   const bool fp8 = cache->desc.cache_dtype == FKV_FP8_E4M3FN;
   // the fused insert exists in the 32-row kernel only (FP8 cache, layout 5, 6 or automatic)
   if (fused_insert && (!fp8 || fkv::split_shape(p.nt, p.layout, fp8).groups_per_cu > -2)) return reject(FKV_EUNSUPPORTED);
+  if (fused_insert && desc->q_len > FKV_MAX_Q_LEN) return reject(FKV_EUNSUPPORTED);  // the kernel stages 16 tokens
   if (desc->num_seqs == 0) return FKV_OK;
   if (fused_insert && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return reject(FKV_EINVAL);
   if (!q || !block_table || !seq_lens || !out) return reject(FKV_EINVAL);

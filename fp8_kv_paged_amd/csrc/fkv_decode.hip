@@ -941,8 +941,9 @@ hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool 
   if (shape.groups_per_cu == 0) {
     e = launch_rows(a, shape.ntw, fp8, stream);
   } else if (shape.groups_per_cu == -2 || shape.groups_per_cu == -3) {
-    // row tiles per work group; layout 6 holds two row tiles per wave
-    e = launch_m32(a, shape.r / a.row_groups, shape.groups_per_cu == -3 ? 2 : 1, a.key_lanes, fp8, stream);
+    // row tiles per work group (rows_pad / 32 row tiles in row_groups groups); layout 6 holds
+    // two row tiles per wave
+    e = launch_m32(a, a.rows_pad / 32 / a.row_groups, shape.groups_per_cu == -3 ? 2 : 1, a.key_lanes, fp8, stream);
   } else if (shape.groups_per_cu < 0) {
     e = launch_wide(a, shape.ntw, fp8, stream);
   } else {

@@ -49,6 +49,7 @@ extern "C" {
 
 #define FKV_HEAD_DIM 128
 #define FKV_MAX_Q_LEN 16
+#define FKV_MAX_PREFILL_Q_LEN 4096
 
 /*
  * Cache geometry. [P2] "Page-32 attention experiment": page (block) sizes 32 and
@@ -131,7 +132,14 @@ int fkv_insert(const fkv_cache* cache, const uint16_t* k, const uint16_t* v, con
  */
 typedef struct fkv_decode_desc {
   int32_t num_seqs;            /* >= 0 (0 = no-op)                                          */
-  int32_t q_len;               /* M, 1..16 query tokens per sequence (q1 = 1, M12 = 12)     */
+  int32_t q_len;               /* M query tokens per sequence (q1 = 1, M12 = 12): 1..16 with
+                                  at most 112 packed rows (Hq/Hkv) * M per KV head; longer
+                                  windows (chunked prefill: the causal attention of up to
+                                  FKV_MAX_PREFILL_Q_LEN new tokens to the cached prefix and
+                                  to each other, [P1] "Initial optimization order" leaves the
+                                  prefill lane for later) with an FP8 cache, layout 0 or 5,
+                                  row_groups 0 and row_exact 0 only (else FKV_EUNSUPPORTED);
+                                  fkv_insert_decode takes at most 16                      */
   int32_t num_q_heads;         /* multiple of num_kv_heads; (Hq/Hkv)*M <= 112               */
   int32_t max_blocks_per_seq;  /* row stride of block_table, >= 1                           */
   int32_t max_seq_len;         /* host upper bound on seq_lens[], sizes the split grid      */

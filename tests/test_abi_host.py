@@ -85,8 +85,9 @@ def test_decode_validation_codes():
     c = _fake_cache()
     assert _ws(c) >= 0
     bad = [
-        (dict(q_len=0), fkv.EINVAL), (dict(q_len=17), fkv.EUNSUPPORTED), (dict(num_q_heads=17), fkv.EINVAL),
-        (dict(num_q_heads=20, q_len=12), fkv.EUNSUPPORTED),  # 10 heads per KV head x 12 rows > 112
+        (dict(q_len=0), fkv.EINVAL), (dict(q_len=4097), fkv.EUNSUPPORTED), (dict(num_q_heads=17), fkv.EINVAL),
+        (dict(q_len=17, layout=3), fkv.EUNSUPPORTED),  # long windows: the 32-row kernel only
+        (dict(num_q_heads=20, q_len=12, layout=1), fkv.EUNSUPPORTED),  # 10 heads per KV head x 12 rows > 112
         (dict(max_seq_len=257), fkv.EINVAL),  # beyond max_blocks_per_seq * block_size
         (dict(max_blocks_per_seq=0), fkv.EINVAL), (dict(num_seqs=-1), fkv.EINVAL),
         (dict(window_left=-2), fkv.EINVAL), (dict(softmax_scale=0.0), fkv.EINVAL),
@@ -226,6 +227,34 @@ def test_bf16_output_plan_rules():
         with pytest.raises(fkv.FkvError) as e:
             _ws(c, **kw, **bad)
         assert e.value.status == fkv.EUNSUPPORTED, bad
+
+
+def test_long_query_window_plan_rules():
+    """Chunked prefill (q_len > 16, or more than 112 packed rows): FP8 cache, layout 0 or 5,
+    automatic row groups, no row-exact mode; ceil(rows / 64) work groups of 64 rows per split,
+    merged by the combine kernel."""
+    c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
+    kw = dict(num_q_heads=72, max_blocks_per_seq=256, max_seq_len=16384)
+    for q_len in (13, 17, 128, 512, 4096):
+        n = _ws(c, q_len=q_len, **kw)
+        assert n == _ws(c, q_len=q_len, layout=5, **kw)
+        rows_pad = (9 * q_len + 63) // 64 * 64
+        ctl = 8 * 256
+        parts = (n - ctl) // (rows_pad * 130 * 4)   # fp32 partial rows plus (m, l) per row
+        assert n == 0 or (parts >= 1 and n - ctl >= parts * rows_pad * 130 * 4), q_len
+    for bad in (dict(layout=3), dict(layout=6), dict(layout=1), dict(row_groups=2), dict(row_exact=1, split_tiles=8)):
+        with pytest.raises(fkv.FkvError) as e:
+            _ws(c, q_len=64, **kw, **bad)
+        assert e.value.status == fkv.EUNSUPPORTED, bad
+    with pytest.raises(fkv.FkvError) as e:
+        _ws(_fake_cache(num_blocks=4096, bs=64, hkv=8, dt="bf16"), q_len=64, **kw)
+    assert e.value.status == fkv.EUNSUPPORTED
+    # the fused insert stages at most 16 tokens
+    L = fkv.lib()
+    dev = ctypes.c_void_p(0x300000)
+    d = fkv.make_decode_desc(1, 17, 72, 256, 16384)
+    assert L.fkv_insert_decode(ctypes.byref(c), ctypes.byref(d), dev, dev, dev, dev, dev, dev, dev, dev, dev, 1 << 30,
+                               None) == fkv.EUNSUPPORTED
 
 
 def test_insert_decode_fails_closed_without_touching_the_gpu():

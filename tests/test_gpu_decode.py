@@ -195,11 +195,21 @@ def test_rows_without_visible_keys_are_zero():
     assert np.all(np.isfinite(out))
 
 
-def test_unsupported_packing_fails_closed():
-    lay = synth.tiny_layer(97, [64], num_q_heads=20, num_kv_heads=2, block_size=32, q_len=12)
+def test_packing_beyond_the_decode_tiles():
+    """10 query heads per KV head x 12 rows = 120 packed rows: more than the row-group, split and
+    wide kernels compile (they fail closed), served by the 32-row kernel's long-window plan."""
+    lay = synth.tiny_layer(97, [64, 700], num_q_heads=20, num_kv_heads=2, block_size=32, q_len=12)
+    for layout in (1, 2, 3, 4):
+        with pytest.raises(fkv.FkvError) as e:
+            PagedLayer(lay, layout=layout)
+        assert e.value.status == fkv.EUNSUPPORTED
+    lay16 = synth.tiny_layer(97, [64], num_q_heads=20, num_kv_heads=2, block_size=32, q_len=12, cache_dtype="bf16")
     with pytest.raises(fkv.FkvError) as e:
-        PagedLayer(lay)
+        PagedLayer(lay16)
     assert e.value.status == fkv.EUNSUPPORTED
+    out = PagedLayer(lay).build().decode().clone()
+    torch.cuda.synchronize()
+    _check(lay, out, label="120 packed rows")
 
 
 def test_fused_split_merge_is_deterministic_and_leaves_counters_zero():

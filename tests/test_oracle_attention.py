@@ -121,6 +121,24 @@ def test_brute_force_tiny(seed):
         assert np.allclose(a, b, rtol=1e-12, atol=1e-12), (Hkv, G, M, L, wl)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_brute_force_long_query_windows(seed):
+    """Chunked prefill: many new rows attend causally to the prefix and to each other."""
+    r = np.random.default_rng(200 + seed)
+    for _ in range(4):
+        Hkv = int(r.choice([1, 2]))
+        G = int(r.choice([1, 9]))
+        M = int(r.choice([17, 33, 64, 130]))
+        L = int(r.integers(M, M + 90))
+        wl = int(r.choice([-1, 7, 40, 511]))
+        q = _rand(r, M, G * Hkv, 128)
+        k = _rand(r, L, Hkv, 128) * 2
+        v = _rand(r, L, Hkv, 128)
+        a = attention.decode_attention(q, k, v, M, wl, S128)
+        b = dense_reference(q, k, v, M, wl, S128)
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12), (Hkv, G, M, L, wl)
+
+
 def test_visible_range_convention():
     # L = 5, one query at position 4, window_left 2 -> keys 2, 3, 4
     assert attention.visible_range(5, 1, 0, 2) == (2, 4)
