@@ -20,6 +20,7 @@ std::atomic<uint64_t> g_split[2][9];
 std::atomic<uint64_t> g_combine;
 std::atomic<uint64_t> g_insert_decode;
 std::atomic<uint64_t> g_norm_rope[2];
+std::atomic<uint64_t> g_norm_rope_decode;
 std::atomic<uint64_t> g_rejected;
 
 int reject(int code) {
@@ -342,9 +343,19 @@ int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* de
   return FKV_OK;
 }
 
+// Q/K RMSNorm + RoPE in front of the fused insert (fkv_norm_rope_insert_decode)
+struct NormRopeIn {
+  const uint16_t* q_w;
+  const uint16_t* k_w;
+  const float* cos_sin;
+  int32_t rope_rows;
+  float eps;
+};
+
 static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q, const uint16_t* k_new,
                        const uint16_t* v_new, const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
-                       const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                       const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                       const NormRopeIn* nr = nullptr) {
   const bool fused_insert = k_new != nullptr;
   fkv::DecodePlan p;
   int rc = plan_decode(cache, desc, &p, fused_insert);
@@ -374,6 +385,10 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   a.v_scale = v_scale;
   a.out = static_cast<float*>(out);
   a.out_bf16 = desc->out_dtype == FKV_OUT_BF16 ? 1 : 0;
+  a.q_w = nr ? nr->q_w : nullptr;
+  a.k_w = nr ? nr->k_w : nullptr;
+  a.cos_sin = nr ? nr->cos_sin : nullptr;
+  a.eps = nr ? nr->eps : 0.f;
   a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
   a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
   a.ws_ctl = p.ws_ctl_bytes ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_ctl_offset) : nullptr;
@@ -404,6 +419,7 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   g_split[fp8 ? 0 : 1][p.nt - 1].fetch_add(1, std::memory_order_relaxed);
   if (combined) g_combine.fetch_add(1, std::memory_order_relaxed);
   if (fused_insert) g_insert_decode.fetch_add(1, std::memory_order_relaxed);
+  if (nr) g_norm_rope_decode.fetch_add(1, std::memory_order_relaxed);
   return FKV_OK;
 }
 
@@ -421,6 +437,21 @@ int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const
   if (!k_new || !v_new) return reject(FKV_EINVAL);
   return decode_call(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, v_scale, out, workspace,
                      workspace_bytes, stream);
+}
+
+int fkv_norm_rope_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                                const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q_weight,
+                                const uint16_t* k_weight, float eps, const float* cos_sin, int32_t rope_rows,
+                                const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                const float* v_scale, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!k_new || !v_new || !desc) return reject(FKV_EINVAL);
+  if (!q_weight || !k_weight || !cos_sin || !aligned(q_weight, 16) || !aligned(k_weight, 16) || !aligned(cos_sin, 16))
+    return reject(FKV_EINVAL);
+  if (!(std::isfinite(eps) && eps >= 0.f) || rope_rows < desc->max_seq_len) return reject(FKV_EINVAL);
+  const NormRopeIn nr{q_weight, k_weight, cos_sin, rope_rows, eps};
+  return decode_call(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, v_scale, out, workspace,
+                     workspace_bytes, stream, &nr);
 }
 
 const char* fkv_status_string(int status) {
@@ -445,6 +476,7 @@ int fkv_get_counters(fkv_counters* out) {
   out->insert_decode_launches = g_insert_decode.load(std::memory_order_relaxed);
   out->rejected_calls = g_rejected.load(std::memory_order_relaxed);
   for (int i = 0; i < 2; ++i) out->norm_rope_insert_launches[i] = g_norm_rope[i].load(std::memory_order_relaxed);
+  out->norm_rope_insert_decode_launches = g_norm_rope_decode.load(std::memory_order_relaxed);
   return FKV_OK;
 }
 
@@ -457,6 +489,7 @@ int fkv_reset_counters(void) {
   g_insert_decode.store(0);
   g_norm_rope[0].store(0);
   g_norm_rope[1].store(0);
+  g_norm_rope_decode.store(0);
   g_rejected.store(0);
   return FKV_OK;
 }

@@ -67,6 +67,67 @@ __device__ __forceinline__ void e4m3_encode8(const u32x4_t& in, float scale, uin
   hi = c[1];
 }
 
+// ---- per-head RMSNorm + rotate-half RoPE in one fixed float32 order ------------------------
+// ("Laguna S 2.1 INT4 -- calibrated FP8 KV on Intel B70", section "Initial optimization
+// order": the scaled insert sits at the Q/K norm + RoPE step.) The order, followed exactly so
+// that BF16 roundings and E4M3 codes are reproducible: each group of 8 consecutive dims sums
+// its squares in dim order; the 16 group sums combine pairwise at group distances 1, 2, 4, 8;
+// r = 1 / sqrt(s / 128 + eps) with the correctly rounded square root (sqrtf here; HIP's
+// __fsqrt_rn maps to the native one) and IEEE division; y = bf16((x r) w); for d < 64,
+// z_d = bf16(y_d c_d - y_(d+64) s_d) and z_(d+64) = bf16(y_(d+64) c_d + y_d s_d), every product
+// and sum rounded on its own (no FMA contraction).
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// One head vector over 16 consecutive lanes, lane c holding dims 8c .. 8c+7 (xin: BF16 x, win:
+// BF16 weights of those dims), row: the position's table row (64 cosines, then 64 sines).
+// Every lane of the wave must call it (16-wide shuffles). Returns the lane's 8 BF16 results.
+__device__ __forceinline__ u32x4_t norm_rope16(const u32x4_t& xin, const u32x4_t& win, int c, float eps,
+                                               const float* row) {
+#pragma clang fp contract(off)
+  float x[8], w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = (j & 1) ? bf16_hi(xin[j >> 1]) : bf16_lo(xin[j >> 1]);
+    w[j] = (j & 1) ? bf16_hi(win[j >> 1]) : bf16_lo(win[j >> 1]);
+  }
+  float s = x[0] * x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) s = s + x[j] * x[j];
+#pragma unroll
+  for (int k = 1; k < 16; k <<= 1) s = s + __shfl_xor(s, k, 16);
+  const float rr = __fdiv_rn(1.0f, sqrtf(__fdiv_rn(s, 128.0f) + eps));
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const uint32_t yb = bf16x2_rne((x[j] * rr) * w[j], (x[j + 1] * rr) * w[j + 1]);
+    y[j] = bf16_lo(yb);
+    y[j + 1] = bf16_hi(yb);
+  }
+  const float* cr = row + 8 * (c & 7);
+  const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cr), c1 = *reinterpret_cast<const f32x4_t*>(cr + 4);
+  const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(cr + 64), s1 = *reinterpret_cast<const f32x4_t*>(cr + 68);
+  const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+  const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  uint32_t zw[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    float z[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float yp = __shfl_xor(y[j + e], 8, 16);  // dim d + 64 (lanes 0-7) or d - 64 (lanes 8-15)
+      const float a0 = y[j + e] * cs[j + e], a1 = yp * sn[j + e];
+      z[e] = c < 8 ? a0 - a1 : a0 + a1;
+    }
+    zw[j >> 1] = bf16x2_rne(z[0], z[1]);
+  }
+  return u32x4_t{zw[0], zw[1], zw[2], zw[3]};
+}
+
 // ---- fp8 -> bf16 / f16 (hardware, exact for every E4M3FN code) -------------------------
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);

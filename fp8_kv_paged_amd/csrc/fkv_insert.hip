@@ -62,14 +62,10 @@ __global__ __launch_bounds__(256) void cache_insert_kernel(InsertArgs a) {
 // section "Initial optimization order": the scaled E4M3 insert at the Q/K norm + RoPE step;
 // "Laguna S 2.1 B70 campaign transfer ledger", section "Result progression and what actually
 // worked": an exact fused Q/K RMSNorm/RoPE stack). Sixteen lanes take one 128-dim head vector
-// of Q or K, 8 consecutive dims each. Every rounding follows one fixed float32 order, with
-// contraction into FMAs switched off: the lane's sum of squares in dim order, a butterfly over
-// the 16 lanes (xor 1, 2, 4, 8), r = 1 / sqrt(s / 128 + eps) with IEEE square root and
-// division, y = bf16((x r) w); the rotate-half partner of dim d < 64 is d + 64, 8 lanes away,
-// z = bf16(y c -/+ y' s). A K row then inserts its z and the token's V row of that head.
+// of Q or K, 8 consecutive dims each (norm_rope16). A K row then inserts its result and the
+// token's V row of that head.
 template <bool kFp8>
 __global__ __launch_bounds__(256) void norm_rope_insert_kernel(NormRopeArgs a) {
-#pragma clang fp contract(off)
   const int rows = a.num_q_heads + a.num_kv_heads;  // normalised head vectors per token
   const int64_t job = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
   const int c = (int)(threadIdx.x & 15);
@@ -82,47 +78,11 @@ __global__ __launch_bounds__(256) void norm_rope_insert_kernel(NormRopeArgs a) {
   const uint16_t* src = is_q ? a.q + (t * a.num_q_heads + h) * kHeadDim : a.k + (t * a.num_kv_heads + h) * kHeadDim;
   const u32x4_t xin = *reinterpret_cast<const u32x4_t*>(src + c * 8);
   const u32x4_t win = *reinterpret_cast<const u32x4_t*>((is_q ? a.q_w : a.k_w) + c * 8);
-  float x[8], w[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    x[j] = __uint_as_float((j & 1) ? (xin[j >> 1] & 0xFFFF0000u) : (xin[j >> 1] << 16));
-    w[j] = __uint_as_float((j & 1) ? (win[j >> 1] & 0xFFFF0000u) : (win[j >> 1] << 16));
-  }
-  float s = x[0] * x[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) s = s + x[j] * x[j];
-#pragma unroll
-  for (int k = 1; k < 16; k <<= 1) s = s + __shfl_xor(s, k, 16);
-  // sqrtf is the correctly rounded square root here (__fsqrt_rn maps to the native one)
-  const float rr = __fdiv_rn(1.0f, sqrtf(__fdiv_rn(s, 128.0f) + a.eps));
-  float y[8];
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    const bf16x2_t yb = __builtin_convertvector(f32x2_t{(x[j] * rr) * w[j], (x[j + 1] * rr) * w[j + 1]}, bf16x2_t);
-    y[j] = (float)yb[0];
-    y[j + 1] = (float)yb[1];
-  }
   const int pos = a.positions[t];
   const bool valid = pos >= 0 && pos < a.rope_rows;
-  const float* row = a.cos_sin + (int64_t)(valid ? pos : 0) * kHeadDim + 8 * (c & 7);
-  const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(row), c1 = *reinterpret_cast<const f32x4_t*>(row + 4);
-  const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(row + 64), s1 = *reinterpret_cast<const f32x4_t*>(row + 68);
-  const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-  const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  uint32_t zw[4];
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    float z[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float yp = __shfl_xor(y[j + e], 8, 16);  // dim d + 64 (lanes 0-7) or d - 64 (lanes 8-15)
-      const float a0 = y[j + e] * cs[j + e], a1 = yp * sn[j + e];
-      z[e] = c < 8 ? a0 - a1 : a0 + a1;
-    }
-    zw[j >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{z[0], z[1]}, bf16x2_t));
-  }
+  const u32x4_t z = norm_rope16(xin, win, c, a.eps, a.cos_sin + (int64_t)(valid ? pos : 0) * kHeadDim);
   if (!live) return;
-  const u32x4_t zb = valid ? u32x4_t{zw[0], zw[1], zw[2], zw[3]} : u32x4_t{0u, 0u, 0u, 0u};
+  const u32x4_t zb = valid ? z : u32x4_t{0u, 0u, 0u, 0u};
   if (is_q) {
     *reinterpret_cast<u32x4_t*>(a.q_out + (t * a.num_q_heads + h) * kHeadDim + c * 8) = zb;
     return;

@@ -67,6 +67,11 @@ struct DecodeArgs {
   int32_t key_lanes;      // 32-row kernel: key lanes per work group
   int32_t align_splits;   // 32-row kernel: splits start at multiples of tiles_per_split (row-exact mode)
   int32_t out_bf16;       // out holds BF16 (rounded to nearest even), else fp32
+  // fused insert with the Q/K RMSNorm + RoPE in front (cos_sin non-null): q and k_new are raw
+  const uint16_t* q_w;    // BF16 [128]
+  const uint16_t* k_w;    // BF16 [128]
+  const float* cos_sin;   // fp32 [rope_rows][128], rope_rows >= max_seq_len
+  float eps;
   float softmax_scale;
 };
 

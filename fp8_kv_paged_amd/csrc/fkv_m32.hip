@@ -298,6 +298,69 @@ __device__ __forceinline__ void quad_finish(const DecodeArgs& a, int b, int g, i
 
 namespace {
 
+// RMSNorm + RoPE (norm_rope16's order) of one query row held by lanes n and n + 32 in the MFMA
+// operand layout: lane half hh holds dims 32j + 16hh .. +15 (j = 0..3) as q[2j] (the first 8)
+// and q[2j + 1], i.e. q[c] holds group g = 4(c / 2) + 2hh + c % 2 of 8 dims. Group distances
+// 1, 4 and 8 stay inside the lane (c xor 1, 2, 4), distance 2 is the lane pair; the rotate-half
+// partner of q[c] (c < 4) is q[c + 4]. Every lane of the wave must call it.
+__device__ __forceinline__ void norm_rope_q64(u32x4_t (&q)[8], const uint16_t* w, int hh, float eps,
+                                              const float* row) {
+#pragma clang fp contract(off)
+  float x[8][8], s[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[c][k] = (k & 1) ? bf16_hi(q[c][k >> 1]) : bf16_lo(q[c][k >> 1]);
+    s[c] = x[c][0] * x[c][0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) s[c] = s[c] + x[c][k] * x[c][k];
+  }
+  float t[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) t[c] = s[c] + s[c ^ 1];  // group distance 1
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s[c] = t[c] + __shfl_xor(t[c], 32);  // distance 2: the lane pair
+#pragma unroll
+  for (int c = 0; c < 8; ++c) t[c] = s[c] + s[c ^ 2];  // distance 4
+#pragma unroll
+  for (int c = 0; c < 8; ++c) s[c] = t[c] + t[c ^ 4];  // distance 8
+  const float rr = __fdiv_rn(1.0f, sqrtf(__fdiv_rn(s[0], 128.0f) + eps));
+  float y[8][8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int g = 4 * (c >> 1) + 2 * hh + (c & 1);
+    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(w + 8 * g);
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const float w0 = bf16_lo(wv[k >> 1]), w1 = bf16_hi(wv[k >> 1]);
+      const uint32_t yb = bf16x2_rne((x[c][k] * rr) * w0, (x[c][k + 1] * rr) * w1);
+      y[c][k] = bf16_lo(yb);
+      y[c][k + 1] = bf16_hi(yb);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int g = 4 * (c >> 1) + 2 * hh + (c & 1);  // dims 8g .. 8g + 7 (< 64), partners in q[c + 4]
+    const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(row + 8 * g);
+    const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(row + 8 * g + 4);
+    const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(row + 64 + 8 * g);
+    const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(row + 64 + 8 * g + 4);
+    const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+    const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float zl[8], zh[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      zl[k] = y[c][k] * cs[k] - y[c + 4][k] * sn[k];
+      zh[k] = y[c + 4][k] * cs[k] + y[c][k] * sn[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      q[c][k >> 1] = bf16x2_rne(zl[k], zl[k + 1]);
+      q[c + 4][k >> 1] = bf16x2_rne(zh[k], zh[k + 1]);
+    }
+  }
+}
+
 template <int RT, int KL, int RW, bool kFp8, bool kIns>
 __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void decode_m32_kernel(DecodeArgs a) {
   typedef M32Shape<RT, KL, RW, kFp8> S;
@@ -448,6 +511,31 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
 #pragma unroll
     for (int u = 0; u < kInsPer; ++u) asm volatile("" : "+v"(nraw[u])::"memory");
     asm volatile("" : "+v"(vs_ins)::"memory");
+  }
+  if constexpr (kIns) {
+    if (a.cos_sin) {
+      // Q/K RMSNorm + RoPE of the raw new tokens, as fkv_qk_norm_rope_insert computes them. New
+      // K rows: 16 consecutive threads per token (the V chunks' threads compute and discard);
+      // table rows are clamped into the table for threads without a token.
+#pragma unroll
+      for (int u = 0; u < kInsPer; ++u) {
+        const int p = min(max(L - M + (ci[u] >> 4), 0), a.max_seq_len - 1);
+        const u32x4_t wk = *reinterpret_cast<const u32x4_t*>(a.k_w + 8 * (ci[u] & 15));
+        const u32x4_t z = norm_rope16(nraw[u], wk, ci[u] & 15, a.eps, a.cos_sin + (int64_t)p * kHeadDim);
+        if (!ins_v_chunk[u]) nraw[u] = z;
+      }
+      // the wave's query rows (padding rows stay zero)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        u32x4_t qn[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qn[c] = qraw[r][c];
+        norm_rope_q64(qn, a.q_w, hh, a.eps, a.cos_sin + (int64_t)max(rpos[r], 0) * kHeadDim);
+        if (rpos[r] >= 0)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) qraw[r][c] = qn[c];
+      }
+    }
   }
   const float C = a.softmax_scale * ks * kLog2e;
   auto block_of = [&](int tile) -> int {

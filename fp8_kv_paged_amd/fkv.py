@@ -50,7 +50,8 @@ class DecodeDesc(ctypes.Structure):
 class Counters(ctypes.Structure):
     _fields_ = [("insert_launches", ctypes.c_uint64 * 2), ("decode_split", (ctypes.c_uint64 * 9) * 2),
                 ("decode_combine_launches", ctypes.c_uint64), ("rejected_calls", ctypes.c_uint64),
-                ("insert_decode_launches", ctypes.c_uint64), ("norm_rope_insert_launches", ctypes.c_uint64 * 2)]
+                ("insert_decode_launches", ctypes.c_uint64), ("norm_rope_insert_launches", ctypes.c_uint64 * 2),
+                ("norm_rope_insert_decode_launches", ctypes.c_uint64)]
 
 
 _lib = None
@@ -74,12 +75,14 @@ def lib():
                                         vp, vp, sz, vp]
         L.fkv_qk_norm_rope_insert.argtypes = [ctypes.POINTER(Cache), i32, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                               i32, vp, vp, vp, vp, vp, vp]
+        L.fkv_norm_rope_insert_decode.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp,
+                                                  ctypes.c_float, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fkv_status_string.argtypes = [ctypes.c_int]
         L.fkv_status_string.restype = ctypes.c_char_p
         L.fkv_get_counters.argtypes = [ctypes.POINTER(Counters)]
         L.fkv_reset_counters.argtypes = []
         for f in ("fkv_cache_bytes", "fkv_init_cache", "fkv_insert", "fkv_decode_workspace_bytes", "fkv_decode_attn",
-                  "fkv_insert_decode", "fkv_qk_norm_rope_insert", "fkv_get_counters", "fkv_reset_counters"):
+                  "fkv_insert_decode", "fkv_qk_norm_rope_insert", "fkv_norm_rope_insert_decode", "fkv_get_counters", "fkv_reset_counters"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -230,6 +233,35 @@ def qk_norm_rope_insert(cache, q, k, v, q_weight, k_weight, eps, cos_sin, positi
            "fkv_qk_norm_rope_insert")
 
 
+def norm_rope_insert_decode(cache, desc, q, k_new, v_new, q_weight, k_weight, eps, cos_sin, block_table, seq_lens,
+                            k_scale, v_scale, out, workspace=None, stream=None):
+    """fkv_norm_rope_insert_decode: insert_decode with raw q / k_new normalised and rotated in the
+    kernel; weights BF16 [128], cos_sin fp32 [P, 128] with P >= desc.max_seq_len."""
+    B, M, Hq = desc.num_seqs, desc.q_len, desc.num_q_heads
+    if q.numel() != B * M * Hq * HEAD_DIM or out.numel() != B * M * Hq * HEAD_DIM:
+        raise ValueError("q / out do not match the decode descriptor")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.numel() != B * M * cache.desc.num_kv_heads * HEAD_DIM:
+            raise ValueError(f"{name} must hold num_seqs x q_len x num_kv_heads x 128 elements")
+    for name, t in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if t.numel() != HEAD_DIM:
+            raise ValueError(f"{name} must hold 128 elements")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
+        raise ValueError("cos_sin must be [rope_rows, 128]")
+    if block_table.numel() != B * desc.max_blocks_per_seq or seq_lens.numel() != B:
+        raise ValueError("block_table / seq_lens do not match the decode descriptor")
+    ws = _ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().fkv_norm_rope_insert_decode(ctypes.byref(cache), ctypes.byref(desc), _ptr(q, "q", 2),
+                                             _ptr(k_new, "k_new", 2), _ptr(v_new, "v_new", 2),
+                                             _ptr(q_weight, "q_weight", 2), _ptr(k_weight, "k_weight", 2),
+                                             float(eps), _ptr(cos_sin, "cos_sin", 4), int(cos_sin.shape[0]),
+                                             _ptr(block_table, "block_table", 4), _ptr(seq_lens, "seq_lens", 4),
+                                             _ptr(k_scale, "k_scale", 4), _ptr(v_scale, "v_scale", 4),
+                                             _ptr(out, "out", _out_size(desc)), ws, ws_bytes, _stream(stream)),
+           "fkv_norm_rope_insert_decode")
+
+
 def get_counters():
     c = Counters()
     _check(lib().fkv_get_counters(ctypes.byref(c)), "fkv_get_counters")
@@ -238,6 +270,7 @@ def get_counters():
             "decode_combine_launches": c.decode_combine_launches,
             "insert_decode_launches": c.insert_decode_launches,
             "norm_rope_insert_launches": list(c.norm_rope_insert_launches),
+            "norm_rope_insert_decode_launches": c.norm_rope_insert_decode_launches,
             "rejected_calls": c.rejected_calls}
 
 

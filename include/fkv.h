@@ -295,6 +295,28 @@ int fkv_qk_norm_rope_insert(const fkv_cache* cache, int32_t num_tokens, int32_t 
                             const int32_t* slot_mapping, const float* k_scale, const float* v_scale, uint16_t* q_out,
                             void* stream);
 
+/*
+ * fkv_insert_decode with the Q/K RMSNorm + RoPE of fkv_qk_norm_rope_insert in front, all in one
+ * launch ([P1] "Initial optimization order": the scaled insert at the Q/K norm + RoPE step,
+ * optionally inside the attention call): q holds the raw query rows and k_new the raw new keys
+ * (as in fkv_insert_decode); each is normalised and rotated in the attention kernel's prologue
+ * with the arithmetic fkv_qk_norm_rope_insert documents, at the row's position L - q_len + i.
+ * The pool bytes and out are bitwise those of fkv_qk_norm_rope_insert (positions L - q_len + i,
+ * the block table's slots) followed by fkv_decode_attn with the rotated Q on layout 5.
+ *
+ *  q_weight, k_weight, eps, cos_sin as fkv_qk_norm_rope_insert; rope_rows >= desc->max_seq_len
+ *  (every position has a table row)
+ *  other arguments as fkv_insert_decode (same rules: FP8 cache, layout 0, 5 or 6, q_len <= 16)
+ * Errors: as fkv_insert_decode, plus FKV_EINVAL for a null or misaligned weight or table, a
+ * negative or non-finite eps, or too few table rows.
+ */
+int fkv_norm_rope_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                                const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q_weight,
+                                const uint16_t* k_weight, float eps, const float* cos_sin, int32_t rope_rows,
+                                const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                const float* v_scale, void* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Human-readable text of a status code (static storage). */
 const char* fkv_status_string(int status);
 
@@ -313,6 +335,8 @@ typedef struct fkv_counters {
   uint64_t insert_decode_launches;  /* fkv_insert_decode calls (also counted in
                                        decode_split)                            */
   uint64_t norm_rope_insert_launches[2];  /* fkv_qk_norm_rope_insert: [0] FP8, [1] BF16 */
+  uint64_t norm_rope_insert_decode_launches;  /* fkv_norm_rope_insert_decode calls (also
+                                                 counted as insert_decode_launches) */
 } fkv_counters;
 
 int fkv_get_counters(fkv_counters* out);

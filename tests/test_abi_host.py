@@ -23,7 +23,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = fkv.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -295,6 +295,26 @@ def test_norm_rope_insert_fails_closed_without_touching_the_gpu():
     assert call(q=ctypes.c_void_p(0x300008)) == fkv.EINVAL  # 16-byte alignment
     assert call(ks=None) == fkv.EINVAL                     # FP8 cache needs the scales
     assert call(T=0) == fkv.OK                             # nothing to do: no launch
+
+
+def test_norm_rope_insert_decode_fails_closed_without_touching_the_gpu():
+    L = fkv.lib()
+    c = _fake_cache()
+    dev = ctypes.c_void_p(0x300000)
+
+    def call(d, qw=dev, eps=1e-6, rows=256, cache=c):
+        return L.fkv_norm_rope_insert_decode(ctypes.byref(cache), ctypes.byref(d), dev, dev, dev, qw, dev,
+                                             ctypes.c_float(eps), dev, rows, dev, dev, dev, dev, dev, dev, 1 << 30,
+                                             None)
+    d = fkv.make_decode_desc(1, 12, 18, 8, 256)
+    assert call(d, qw=None) == fkv.EINVAL
+    assert call(d, qw=ctypes.c_void_p(0x300004)) == fkv.EINVAL
+    assert call(d, eps=-1.0) == fkv.EINVAL
+    assert call(d, rows=255) == fkv.EINVAL          # a position without a table row
+    d.layout = 3
+    assert call(d) == fkv.EUNSUPPORTED               # the 32-row kernel only
+    assert call(fkv.make_decode_desc(1, 12, 18, 8, 256), cache=_fake_cache(dt="bf16")) == fkv.EUNSUPPORTED
+    assert call(fkv.make_decode_desc(0, 12, 18, 8, 256)) == fkv.OK  # no sequences: no launch
 
 
 def test_counters_record_rejections():

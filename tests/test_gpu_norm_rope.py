@@ -135,3 +135,72 @@ def test_decode_attention_after_the_step(label, make):
     worst = float(parity.row_errors(out.cpu().numpy(), ref).max())
     print(f"[norm_rope_insert + decode] {label}: max row error {worst:.3e}", flush=True)
     assert worst <= parity.ATTN_TOL, (label, worst)
+
+
+def _fused_cases():
+    yield "c3 8k page 64", lambda: synth.c3_layer(8192, 64), {}
+    yield "c2 window 512", synth.c2_layer, {}
+    yield "ragged, rows before position 0", \
+        lambda: synth.tiny_layer(521, [40, 5, 700, 12], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12), {}
+    yield "q1 batch of 24, 72/8", lambda: synth.tiny_layer(523, list(range(1, 1200, 50)), num_q_heads=72,
+                                                            num_kv_heads=8, block_size=64, q_len=1), {}
+    yield "c3 8k page 64, layout 6", lambda: synth.c3_layer(8192, 64), {"layout": 6}
+
+
+@pytest.mark.parametrize("label,make,kw", list(_fused_cases()), ids=[c[0] for c in _fused_cases()])
+def test_norm_rope_inside_the_attention_launch(label, make, kw):
+    """fkv_norm_rope_insert_decode equals fkv_qk_norm_rope_insert followed by fkv_decode_attn with
+    the rotated Q (same layout; layout 5 for the automatic one) bit for bit: pools and output."""
+    lay = make()
+    st = synth.norm_rope_step(lay)
+    dev = "cuda"
+    q, k, v = (to_dev_bits(x, dev) for x in (st.q_bits, st.k_bits, st.v_bits))
+    qw, kw_ = to_dev_bits(st.q_w, dev), to_dev_bits(st.k_w, dev)
+    cs = torch.from_numpy(st.cos_sin).to(dev)
+
+    fused = PagedLayer(lay, **kw)
+    fused.prefill()
+    before = fkv.get_counters()
+    fkv.norm_rope_insert_decode(fused.cache, fused.ddesc, q, k, v, qw, kw_, st.eps, cs, fused.block_table,
+                                fused.seq_lens, fused.k_scale, fused.v_scale, fused.out, fused.workspace)
+    out_f = fused.out.clone()
+
+    sep = PagedLayer(lay, layout=kw.get("layout", 5))
+    sep.prefill()
+    q_rot = torch.empty_like(q)
+    fkv.qk_norm_rope_insert(sep.cache, q, k, v, qw, kw_, st.eps, cs, torch.from_numpy(st.positions).to(dev),
+                            torch.from_numpy(st.slot_mapping).to(dev), sep.k_scale, sep.v_scale, q_rot)
+    sep.q = q_rot.view(lay.num_seqs, lay.q_len, lay.num_q_heads, 128)
+    out_s = sep.decode().clone()
+    torch.cuda.synchronize()
+    after = fkv.get_counters()
+    assert after["norm_rope_insert_decode_launches"] == before["norm_rope_insert_decode_launches"] + 1
+    assert torch.equal(fused.k_pool, sep.k_pool), f"{label}: K pool differs"
+    assert torch.equal(fused.v_pool, sep.v_pool), f"{label}: V pool differs"
+    assert torch.equal(out_f, out_s), f"{label}: output differs from the two-launch path"
+    print(f"[norm_rope_insert_decode] {label}: bitwise equal to norm_rope_insert + decode", flush=True)
+
+
+def test_norm_rope_inside_the_attention_launch_against_the_oracle():
+    lay = synth.c2_layer()
+    st = synth.norm_rope_step(lay)
+    dev = "cuda"
+    gl = PagedLayer(lay)
+    gl.prefill()
+    fkv.norm_rope_insert_decode(gl.cache, gl.ddesc, *(to_dev_bits(x, dev) for x in (st.q_bits, st.k_bits, st.v_bits)),
+                                to_dev_bits(st.q_w, dev), to_dev_bits(st.k_w, dev), st.eps,
+                                torch.from_numpy(st.cos_sin).to(dev), gl.block_table, gl.seq_lens, gl.k_scale,
+                                gl.v_scale, gl.out, gl.workspace)
+    out = gl.out.clone()
+    torch.cuda.synchronize()
+    kp, vp = _oracle_prefilled(lay)
+    q_ref = normrope.norm_rope_insert(kp, vp, st.q_bits, st.k_bits, st.v_bits, st.q_w, st.k_w, st.eps, st.cos_sin,
+                                      st.positions, st.slot_mapping, lay.k_scale, lay.v_scale, lay.block_size,
+                                      lay.num_kv_heads)
+    assert np.array_equal(gl.k_pool.cpu().numpy(), kp) and np.array_equal(gl.v_pool.cpu().numpy(), vp)
+    ref = attention.paged_decode(kp, vp, q_ref.reshape(lay.num_seqs, lay.q_len, lay.num_q_heads, 128),
+                                 lay.block_table, lay.seq_lens, lay.q_len, lay.window_left, lay.softmax_scale,
+                                 lay.k_scale, lay.v_scale, lay.block_size, lay.num_kv_heads, lay.cache_dtype)
+    worst = float(parity.row_errors(out.cpu().numpy(), ref).max())
+    print(f"[norm_rope_insert_decode] c2 against the oracle: max row error {worst:.3e}", flush=True)
+    assert worst <= parity.ATTN_TOL
