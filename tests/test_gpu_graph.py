@@ -85,3 +85,52 @@ def test_decode_graph_with_split_merge_counters():
         torch.cuda.synchronize()
         assert torch.equal(gl.out, ref), rep
         assert torch.count_nonzero(gl.workspace[nws - ctl:nws]).item() == 0, rep
+
+
+def test_norm_rope_paths_in_a_graph():
+    """The Q/K norm + RoPE entry points captured in one graph per layer: the standalone step
+    followed by decode on one layer, the step inside the attention launch on another. Each
+    replay (with eager work and synchronisations in between) reproduces the eager outputs,
+    rotated Q and pool bytes bit for bit."""
+    from fp8_kv_paged_amd.layer import to_dev_bits
+    lay = synth.c4_layer(3)
+    st = synth.norm_rope_step(lay)
+    d = "cuda"
+    q, k, v = (to_dev_bits(x, d) for x in (st.q_bits, st.k_bits, st.v_bits))
+    qw, kw = to_dev_bits(st.q_w, d), to_dev_bits(st.k_w, d)
+    cs = torch.from_numpy(st.cos_sin).to(d)
+    pos, sl = torch.from_numpy(st.positions).to(d), torch.from_numpy(st.slot_mapping).to(d)
+    two, one = PagedLayer(lay, layout=5), PagedLayer(lay)
+    for gl in (two, one):
+        gl.prefill()
+    q_rot = torch.empty_like(q)
+    two.q = q_rot.view(lay.num_seqs, lay.q_len, lay.num_q_heads, 128)
+    stream = torch.cuda.Stream()
+
+    def step(s):
+        fkv.qk_norm_rope_insert(two.cache, q, k, v, qw, kw, st.eps, cs, pos, sl, two.k_scale, two.v_scale, q_rot, s)
+        two.decode(s)
+        fkv.norm_rope_insert_decode(one.cache, one.ddesc, q, k, v, qw, kw, st.eps, cs, one.block_table, one.seq_lens,
+                                    one.k_scale, one.v_scale, one.out, one.workspace, s)
+    with torch.cuda.stream(stream):
+        step(stream)
+    stream.synchronize()
+    ref = [two.out.clone(), one.out.clone(), q_rot.clone(), two.k_pool.clone(), one.k_pool.clone(),
+           one.v_pool.clone()]
+    assert torch.equal(ref[0], ref[1]) and torch.equal(ref[3], ref[4])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step(stream)
+    torch.cuda.synchronize()
+    nws = fkv.decode_workspace_bytes(one.cache, one.ddesc)
+    ctl = lay.num_seqs * lay.num_kv_heads * 256
+    for rep in range(3):
+        for t in (two.out, one.out, q_rot):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [two.out, one.out, q_rot, two.k_pool, one.k_pool, one.v_pool]
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), rep
+        assert torch.count_nonzero(one.workspace[nws - ctl:nws]).item() == 0, rep
+    print("[graph] norm/RoPE paths: 3 replays equal to eager", flush=True)
