@@ -1,17 +1,20 @@
 """Benchmark of the calibrated-FP8 paged KV hot path on one MI355X.
 
 One step = one layer call of the full path on the 72-query / 8-KV-head layer at
-context 8,192 with a 12-token causal verify window (M=12), global attention:
-insert the 12 new BF16 K/V tokens into the FP8 cache (E4M3 with per-tensor
-scales), then paged GQA decode attention over the FP8 pages (split-KV kernel +
-cross-split combine). Steps rotate over enough distinct layer copies (different
-pools, identical contents) that the working set exceeds the 256 MB Infinity
-Cache, so KV reads come from HBM.
+context 8,192 with a 12-token causal verify window (M=12), global attention, page
+64: the 12 new BF16 K/V tokens inserted into the FP8 cache (E4M3 with per-tensor
+scales) and paged GQA decode attention over the FP8 pages, in one
+fkv_insert_decode launch (split partials merged inside the kernel). The timed steps
+are replayed from one captured HIP graph and checked bit for bit against the eager
+steps; they rotate over enough distinct layer copies (different pools, identical
+contents) that the working set exceeds the 256 MB Infinity Cache, so K/V comes
+from HBM. Insert and decode as two launches are timed beside it.
 
-Prints ONE JSON line. `value` is KV-read throughput of the whole step
-(algorithmic KV bytes / step time); the decode pair alone is reported as
-`roofline` (bound: HBM) with its achieved bandwidth from HIP events recorded
-on the launch stream; `cpu_baseline` times the NumPy oracle on host cores.
+Prints ONE JSON line. `value` is K/V-read throughput of the whole step
+(algorithmic K/V bytes / step time); `roofline` is that kernel's HBM roofline
+(achieved bandwidth from HIP events on its launch stream, traffic from the
+committed rocprofv3 counter summary when it was taken on this source);
+`cpu_baseline` times the NumPy oracle on host cores.
 """
 
 import argparse
@@ -45,7 +48,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--ab", action="store_true", help="also time the page-size A/B and 32k context")
     p.add_argument("--suite", action="store_true",
-                   help="also time the other workloads (C1, C2, the C4 cycle eager and as a HIP graph, C5)")
+                   help="also time the other workloads (C1, C2, the C4 cycle eager and as a HIP graph, C5, "
+                        "the Q/K norm + RoPE step and a 512-token prefill chunk); no CPU baseline")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run device-to-device copies of MIB MiB (scales the HBM byte counters)")
     return p.parse_args()
@@ -207,9 +211,10 @@ def _visible_kv_bytes(lay, elem):
 
 
 def run_suite(iters):
-    """The other workloads of the scope table, timed with HIP events (median):
-    C1 / C2 single layers, the 54-layer C4 cycle eager and as a captured HIP graph, and the
-    32-sequence C5 batch with FP8 and BF16 caches at M = 1 and 12."""
+    """The other workloads of the scope table, timed with HIP events (median): the Q/K norm +
+    RoPE + insert step and a 512-token prefill chunk of the 72/8 layer, C1 / C2 single layers,
+    the 54-layer C4 cycle eager and as a captured HIP graph, and the 32-sequence C5 batch with
+    FP8 and BF16 caches at M = 1 and 12. Each section prints a progress line on stderr."""
     import torch
     from fp8_kv_paged_amd import synth
     from fp8_kv_paged_amd.layer import PagedLayer
