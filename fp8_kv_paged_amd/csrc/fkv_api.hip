@@ -108,6 +108,7 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   p->row_groups = 1;
   p->key_lanes = 0;
   p->align_splits = 0;
+  p->clip_rows = long_rows ? 1 : 0;
   if (d->row_exact && (!fp8 || (layout != 0 && layout != 5))) return FKV_EUNSUPPORTED;
   int64_t tps = d->split_tiles;
   if (sh.groups_per_cu == -2 || sh.groups_per_cu == -3) {
@@ -410,6 +411,7 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   a.row_groups = p.row_groups;
   a.key_lanes = p.key_lanes;
   a.align_splits = p.align_splits;
+  a.clip_rows = p.clip_rows;
   a.softmax_scale = desc->softmax_scale;
   bool combined = false;
   const hipError_t e = fkv::launch_decode(a, fkv::split_shape(p.nt, p.layout, fp8), fp8, static_cast<hipStream_t>(stream),

@@ -41,6 +41,7 @@ struct DecodePlan {
   int fused_combine;   // layout 5 with the whole grid resident: splits merged inside the kernel
   int key_lanes;       // 32-row kernel: key lanes per work group
   int align_splits;    // 32-row kernel, row-exact mode: split boundaries at absolute tile indices
+  int clip_rows;       // 32-row kernel, long query windows: per-work-group key ranges
   int xcd_pairs;       // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
   size_t ws_bytes;     // total, 256-byte aligned pieces
 };
@@ -66,6 +67,7 @@ struct DecodeArgs {
   int32_t fused_combine;  // 32-row kernel: merge the splits inside the kernel (no combine launch)
   int32_t key_lanes;      // 32-row kernel: key lanes per work group
   int32_t align_splits;   // 32-row kernel: splits start at multiples of tiles_per_split (row-exact mode)
+  int32_t clip_rows;      // 32-row kernel, long query windows: each work group skips the tiles its rows cannot see
   int32_t out_bf16;       // out holds BF16 (rounded to nearest even), else fp32
   // fused insert with the Q/K RMSNorm + RoPE in front (cos_sin non-null): q and k_new are raw
   const uint16_t* q_w;    // BF16 [128]

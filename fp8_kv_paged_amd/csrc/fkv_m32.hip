@@ -440,8 +440,22 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   const int group_wgs = nsplit * RG;  // work groups that write partials of this pair
   if (fused && threadIdx.x == 0)
     __hip_atomic_fetch_add(&ctl[kCtlStarted], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int tb = t_base + s * tps;
-  const int te = min(tb + tps, t_end);
+  int tb = t_base + s * tps;
+  int te = min(tb + tps, t_end);
+  if (a.clip_rows) {
+    // long query windows: only the tiles some row of this work group can see (past its last
+    // row's position, or before its first row's window, every key is masked for all its rows).
+    // The start moves by whole steps of KL tiles, so every tile keeps its key lane and the
+    // result is bitwise that of the full range; an empty range still writes its split partial
+    // (l = 0).
+    const int p_lo = L - M + row0 / G;
+    const int p_hi = L - M + (min(row0 + kRows, GM) - 1) / G;
+    te = max(tb, min(te, p_hi < 0 ? 0 : p_hi / kTile + 1));
+    if (wl >= 0) {
+      const int t_lo = min(te, max(0, p_lo - wl) / kTile);
+      if (t_lo > tb) tb += (t_lo - tb) / KL * KL;
+    }
+  }
   if (wl >= 0) {
     lb0 = tb >> bshift;
     if (lb0 + lane < a.max_blocks) bt_lo = btrow[lb0 + lane];
