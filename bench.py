@@ -176,7 +176,7 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
     nt = (72 // 8 * args.q_len + 15) // 16
     fused_calls = 2 * steps + warmup if fused_ok else 0  # eager steps, then the captured ones
     calls = steps + warmup + fused_calls
-    assert cnt["decode_split"][0 if cache_dtype == "fp8_e4m3fn" else 1][nt - 1] == calls, cnt
+    assert cnt["decode_row_tiles"][0 if cache_dtype == "fp8_e4m3fn" else 1][nt - 1] == calls, cnt
     assert cnt["insert_decode_launches"] == fused_calls, cnt
     res.update(step_ms=mean(step_ms), insert_ms=mean(ins_ms), decode_ms=mean(dec_ms), decode_ms_median=med(dec_ms),
                combine=cnt["decode_combine_launches"] > 0, fused=cnt["decode_combine_launches"] == 0)
@@ -391,8 +391,7 @@ def cpu_baseline(seconds):
 
 
 # split kernel each decode layout launches (layout 0, the automatic choice, is the 32-row kernel for FP8)
-DECODE_KERNELS = {0: "decode_m32_kernel", 1: "decode_split_dma_kernel", 2: "decode_split_kernel",
-                  3: "decode_rows_kernel", 4: "decode_wide_kernel", 5: "decode_m32_kernel", 6: "decode_m32_kernel"}
+DECODE_KERNELS = {0: "decode_m32_kernel", 3: "decode_rows_kernel", 5: "decode_m32_kernel", 6: "decode_m32_kernel"}
 
 
 def source_hash():

@@ -16,12 +16,21 @@ constexpr int kMaxSplitTiles = 1 << 20;
 constexpr uint64_t kAlign = 256;
 
 std::atomic<uint64_t> g_insert[2];
-std::atomic<uint64_t> g_split[2][9];
+std::atomic<uint64_t> g_decode[2];                // decode launches by cache type (0 = FP8, 1 = BF16)
+std::atomic<uint64_t> g_decode_tiles[2][kMaxNT];  // decode shapes: [cache][query row tiles - 1]
+std::atomic<uint64_t> g_long_window[2];           // long query windows (chunked prefill)
 std::atomic<uint64_t> g_combine;
 std::atomic<uint64_t> g_insert_decode;
 std::atomic<uint64_t> g_norm_rope[2];
 std::atomic<uint64_t> g_norm_rope_decode;
 std::atomic<uint64_t> g_rejected;
+
+// Counter slot of a decode launch: nt - 1 for the decode shapes (1 <= nt <= kMaxNT query row
+// tiles of 16 and q_len <= FKV_MAX_Q_LEN), -1 for long query windows, which have no per-shape
+// slot. Every index into g_decode_tiles comes from here.
+int decode_tile_slot(int nt, int q_len) {
+  return (nt >= 1 && nt <= kMaxNT && q_len >= 1 && q_len <= FKV_MAX_Q_LEN) ? nt - 1 : -1;
+}
 
 int reject(int code) {
   g_rejected.fetch_add(1, std::memory_order_relaxed);
@@ -72,15 +81,13 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   if (d->num_seqs < 0 || d->q_len < 1 || d->num_q_heads < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 1)
     return FKV_EINVAL;
   if (d->window_left < -1 || d->split_tiles < 0 || d->split_tiles > kMaxSplitTiles) return FKV_EINVAL;
-  if (layout < 0 || layout > 6) return FKV_EINVAL;
+  if (layout != 0 && layout != 3 && layout != 5 && layout != 6) return FKV_EINVAL;
   if (d->row_exact && (d->split_tiles == 0 || d->split_tiles % 4 != 0)) return FKV_EINVAL;
   if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return FKV_EINVAL;
   if (d->num_q_heads % hkv != 0) return FKV_EINVAL;
   if ((int64_t)d->max_seq_len > (int64_t)d->max_blocks_per_seq * c->desc.block_size) return FKV_EINVAL;
   if (d->q_len > FKV_MAX_PREFILL_Q_LEN) return FKV_EUNSUPPORTED;
   if (d->out_dtype != FKV_OUT_F32 && d->out_dtype != FKV_OUT_BF16) return FKV_EUNSUPPORTED;
-  // BF16 output: the row-group and 32-row kernels and their merges (layouts 1, 2 and 4 write fp32 only)
-  if (d->out_dtype == FKV_OUT_BF16 && (layout == 1 || layout == 2 || layout == 4)) return FKV_EUNSUPPORTED;
   if (d->num_seqs > 65535) return FKV_EUNSUPPORTED;
   const int64_t group = d->num_q_heads / hkv;
   const int64_t rows = group * d->q_len;
@@ -90,7 +97,6 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
   if (long_rows && !(c->desc.cache_dtype == FKV_FP8_E4M3FN && (layout == 0 || layout == 5) && !d->row_exact &&
                      d->row_groups == 0))
     return FKV_EUNSUPPORTED;
-  if (layout == 4 && nt < 3) return FKV_EUNSUPPORTED;  // the wide kernel needs two row halves
   const bool fp8_cache = c->desc.cache_dtype == FKV_FP8_E4M3FN;
   if ((layout == 5 || layout == 6) && !fp8_cache) return FKV_EUNSUPPORTED;  // the 32-row kernel reads FP8 caches
   p->nt = nt;
@@ -156,41 +162,30 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
       tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
     }
     if (tps > fkv::kMaxDmaSplitTiles) return FKV_EUNSUPPORTED;  // the page-table window holds 128 entries
-  } else if (sh.groups_per_cu <= 0) {
-    // row-group (0) and wide (-1) kernels: one work group per CU; the row groups of a KV
-    // head multiply the work groups (the wide kernel keeps both row halves in one), the
-    // splits fill the rest of the chip
+  } else {
+    // row-group kernel (layout 3): one work group per CU; the row groups of a KV head
+    // multiply the work groups, the splits fill the rest of the chip
     p->row_groups = sh.r;
     p->rows_pad = 16 * sh.ntw * sh.r;
     if (tps == 0) {
       const int64_t bg = (int64_t)std::max(d->num_seqs, 1) * hkv;
-      const int64_t wgs = sh.groups_per_cu == 0 ? sh.r : 1;  // work groups per split
-      const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * wgs));
+      const int64_t splits = std::max<int64_t>(1, kNumCUs / (bg * sh.r));
       tps = (tiles_max + splits - 1) / splits;
       tps = (tps + sh.k - 1) / sh.k * sh.k;  // whole tiles for every wave
       tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
       tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
     }
-  } else if (tps == 0) {
-    // Fill the chip: every key lane of every resident group takes at least one tile, a
-    // group at most 128 so a long sequence still spreads over many CUs.
-    const int64_t lanes = (int64_t)kNumCUs * sh.groups_per_cu * sh.k;
-    const int64_t units = (int64_t)std::max(d->num_seqs, 1) * hkv * tiles_max;
-    const int64_t per_lane = std::max<int64_t>(1, (units + lanes - 1) / lanes);
-    tps = std::min<int64_t>(128, sh.k * per_lane);
-    tps = std::max<int64_t>(tps, (tiles_max + fkv::kMaxSplits - 1) / fkv::kMaxSplits);
-    if (sh.ntw <= 2) tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
+    if (tps > fkv::kMaxDmaSplitTiles) return FKV_EUNSUPPORTED;  // its page-table window holds 128 entries
   }
-  if (sh.ntw <= 2 && tps > fkv::kMaxDmaSplitTiles) return FKV_EUNSUPPORTED;
   // aligned splits (row-exact mode) can straddle one more split boundary inside a window
   const int64_t max_splits = (tiles_max + tps - 1) / tps + (p->align_splits && d->window_left >= 0 ? 1 : 0);
   if (max_splits > fkv::kMaxSplits) return FKV_EUNSUPPORTED;
   if ((int64_t)std::max(d->num_seqs, 1) * hkv * max_splits * p->row_groups > 0x7FFFFFFF) return FKV_EUNSUPPORTED;
   p->tiles_per_split = (int)tps;
   p->max_splits = (int)max_splits;
-  // Row-group kernel: with at least eight (sequence, KV head) pairs, each pair's work groups
-  // go to one XCD (all eight XCDs stay busy); else each split's row groups share one.
-  p->xcd_pairs = ((sh.groups_per_cu == 0 || sh.groups_per_cu <= -2) && (int64_t)std::max(d->num_seqs, 1) * hkv >= 8) ? 1 : 0;
+  // With at least eight (sequence, KV head) pairs, each pair's work groups go to one XCD (all
+  // eight XCDs stay busy); else each split's row groups share one.
+  p->xcd_pairs = (int64_t)std::max(d->num_seqs, 1) * hkv >= 8 ? 1 : 0;
   p->fused_combine = 0;
   p->ws_ctl_bytes = 0;
   if (max_splits <= 1) {
@@ -418,7 +413,13 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
                                           &combined);
   if (e == hipErrorInvalidValue) return reject(FKV_EUNSUPPORTED);
   if (e != hipSuccess) return reject(FKV_EHIP);
-  g_split[fp8 ? 0 : 1][p.nt - 1].fetch_add(1, std::memory_order_relaxed);
+  const int ci = fp8 ? 0 : 1;
+  g_decode[ci].fetch_add(1, std::memory_order_relaxed);
+  const int slot = decode_tile_slot(p.nt, desc->q_len);
+  if (slot >= 0)
+    g_decode_tiles[ci][slot].fetch_add(1, std::memory_order_relaxed);
+  else
+    g_long_window[ci].fetch_add(1, std::memory_order_relaxed);
   if (combined) g_combine.fetch_add(1, std::memory_order_relaxed);
   if (fused_insert) g_insert_decode.fetch_add(1, std::memory_order_relaxed);
   if (nr) g_norm_rope_decode.fetch_add(1, std::memory_order_relaxed);
@@ -472,7 +473,9 @@ int fkv_get_counters(fkv_counters* out) {
   std::memset(out, 0, sizeof(*out));
   for (int i = 0; i < 2; ++i) {
     out->insert_launches[i] = g_insert[i].load(std::memory_order_relaxed);
-    for (int j = 0; j < 9; ++j) out->decode_split[i][j] = g_split[i][j].load(std::memory_order_relaxed);
+    out->decode_launches[i] = g_decode[i].load(std::memory_order_relaxed);
+    for (int j = 0; j < kMaxNT; ++j) out->decode_row_tiles[i][j] = g_decode_tiles[i][j].load(std::memory_order_relaxed);
+    out->decode_long_windows[i] = g_long_window[i].load(std::memory_order_relaxed);
   }
   out->decode_combine_launches = g_combine.load(std::memory_order_relaxed);
   out->insert_decode_launches = g_insert_decode.load(std::memory_order_relaxed);
@@ -485,7 +488,9 @@ int fkv_get_counters(fkv_counters* out) {
 int fkv_reset_counters(void) {
   for (int i = 0; i < 2; ++i) {
     g_insert[i].store(0);
-    for (int j = 0; j < 9; ++j) g_split[i][j].store(0);
+    g_decode[i].store(0);
+    for (int j = 0; j < kMaxNT; ++j) g_decode_tiles[i][j].store(0);
+    g_long_window[i].store(0);
   }
   g_combine.store(0);
   g_insert_decode.store(0);

@@ -6,7 +6,6 @@
 
 namespace fkv {
 
-constexpr int kWaves = 4;        // waves per decode work group
 constexpr int kMaxSplits = 512;  // split-KV partials per (sequence, KV head) the combine can merge
 constexpr int kMaxDmaSplitTiles = 128;  // 32-key tiles per split of the LDS-pipelined kernels
 constexpr int kFastMergeSplits = 16;    // 32-row kernel: splits one thread merges with all loads in flight
@@ -62,8 +61,8 @@ struct DecodeArgs {
   uint32_t* ws_ctl;      // 64 words per (sequence, KV head): merge counters and claim bits
   int32_t num_seqs, num_q_heads, num_kv_heads, group, q_len, block_size, max_blocks, num_blocks;
   int32_t window_left, tiles_per_split, max_splits, max_seq_len, rows_pad;
-  int32_t row_groups;  // row-group kernel: groups of 16*ntw packed rows
-  int32_t xcd_pairs;   // row-group kernel: each (sequence, KV head) pair's work groups on one XCD
+  int32_t row_groups;  // work groups per (sequence, KV head, split) sharing its query rows
+  int32_t xcd_pairs;   // each (sequence, KV head) pair's work groups on one XCD
   int32_t fused_combine;  // 32-row kernel: merge the splits inside the kernel (no combine launch)
   int32_t key_lanes;      // 32-row kernel: key lanes per work group
   int32_t align_splits;   // 32-row kernel: splits start at multiples of tiles_per_split (row-exact mode)
@@ -98,25 +97,14 @@ struct NormRopeArgs {
   float eps;
 };
 hipError_t launch_norm_rope_insert(const NormRopeArgs& a, bool fp8, hipStream_t stream);
-// Work-group shape of the split kernel: R row groups of NTW row tiles each, K key lanes
-// per group (R*K waves), and how many such groups one CU holds at once.
+// Work-group shape of a decode kernel: r row groups of ntw row tiles each, k key lanes per
+// group, and groups_per_cu marking the kernel: 0 = the row-group kernel (layout 3; 16-row
+// tiles, ntw of them per group), -2 = the 32-row kernel (layout 5; ntw = r row tiles of 32,
+// k = 8 / r key lanes), -3 = the 32-row kernel with two row tiles per wave (layout 6, k = 4).
 struct SplitShapeInfo {
   int ntw, r, k, groups_per_cu;
 };
 
-// layout 1: row groups of at most two 16-row tiles per wave, two waves per SIMD, so one
-// wave's MFMA work overlaps another's softmax; layout 2: one group holding every row
-// tile, one wave per SIMD, each K/V byte converted once.
-// Layout 3: row groups of ntw tiles in separate work groups of K waves each (groups_per_cu
-// 0 marks it), one work group per CU.
-// Layout 4: one work group of four waves per (sequence, KV head, split), the rows cut into
-// two halves of ntw tiles and the keys into two lanes (groups_per_cu -1 marks it); r = 2
-// row halves, k = 2 key lanes.
-// Layout 5 (FP8 cache): one work group of eight waves per (sequence, KV head, split), the
-// rows cut into r tiles of 32 (1, 2 or 4) and the keys into k = 8 / r lanes
-// (groups_per_cu -2 marks it; ntw = r). Layout 6 (FP8 cache, at least two row tiles): the
-// same plan with two row tiles per work group held by each of its four waves (one per SIMD,
-// k = 4 key lanes); groups_per_cu -3 marks it.
 inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
   if (layout == 5 || layout == 6 || (layout == 0 && fp8)) {  // layout 0 (automatic) is layout 5 for FP8 caches
     const int rows = 16 * nt;
@@ -124,15 +112,9 @@ inline SplitShapeInfo split_shape(int nt, int layout, bool fp8 = true) {
     if (layout == 6) return {rt, rt, 4, -3};
     return {rt, rt, 8 / rt, -2};
   }
-  if (layout == 4 && nt >= 3) return {(nt + 1) / 2, 2, 2, -1};
-  if (layout == 3 || layout == 0) {  // layout 0 (automatic) is layout 3 for BF16 caches
-    const int ntw = nt >= 2 ? 2 : 1;
-    return {ntw, (nt + ntw - 1) / ntw, fp8 ? 8 : 4, 0};
-  }
-  if (layout == 2 && nt >= 3) return {nt, 1, 4, 1};
-  if (nt <= 2) return {nt, 1, 4, 2};
-  if (nt <= 4) return {2, 2, 4, 1};
-  return {2, 4, 2, 1};
+  // layout 3, and layout 0 (automatic) for BF16 caches
+  const int ntw = nt >= 2 ? 2 : 1;
+  return {ntw, (nt + ntw - 1) / ntw, fp8 ? 8 : 4, 0};
 }
 
 // Row-group split kernel (layout 3): ntw 16-row tiles per row group.
@@ -140,10 +122,6 @@ hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t strea
 // 32-row tile kernel: rt row tiles of 32 per work group (1, 2 or 4) and rw per wave (layout 5:
 // 1; layout 6: 2 with rt = 2), FP8 cache only.
 hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, int kl, bool fp8, hipStream_t stream);
-// Wide split kernel (layout 4): ntw 16-row tiles per row half.
-hipError_t launch_wide(const DecodeArgs& a, int ntw, bool fp8, hipStream_t stream);
-// Merges the wide kernel's lane-layout split partials into out.
-hipError_t launch_combine_lanes(const DecodeArgs& a, bool fp8, hipStream_t stream);
 // Merges split partials (rows_pad rows per partial) into out.
 hipError_t launch_combine(const DecodeArgs& a, bool fp8, hipStream_t stream);
 

@@ -114,23 +114,4 @@ __device__ __forceinline__ void dma_tile(const unsigned char* kb, const unsigned
   for (int j = 0; j < kHalf; ++j) __builtin_amdgcn_global_load_lds(vb + 16 * j, dst + (kHalf + j) * 1024, 16, 0, 0);
 }
 
-// O^T += V^T P^T with the accumulator held in AGPRs. The compiler keeps a register
-// array that only inline asm reads and writes in the AGPR file; left to itself it runs
-// these MFMAs in VGPR form and moves every accumulator in and out of AGPRs on each tile.
-// The asm carries the wait states its inputs need: two after a VALU write of a source
-// VGPR (the hazard recognizer does not look into inline asm).
-__device__ __forceinline__ void pv_f16(f32x4_t& acc, const f16x8_t& a, const f16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void pv_bf16(f32x4_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// Orders every later access of one row tile's accumulators after the MFMAs in flight on
-// them (an MFMA result may be read by other instructions only 18 wait states after the
-// MFMA issues), and every later MFMA after earlier VALU writes of them.
-__device__ __forceinline__ void acc_fence(f32x4_t (&o)[8]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4"
-               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]), "+a"(o[6]), "+a"(o[7]));
-}
-
 }  // namespace fkv

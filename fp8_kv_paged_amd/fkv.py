@@ -48,7 +48,8 @@ class DecodeDesc(ctypes.Structure):
 
 
 class Counters(ctypes.Structure):
-    _fields_ = [("insert_launches", ctypes.c_uint64 * 2), ("decode_split", (ctypes.c_uint64 * 9) * 2),
+    _fields_ = [("insert_launches", ctypes.c_uint64 * 2), ("decode_launches", ctypes.c_uint64 * 2),
+                ("decode_row_tiles", (ctypes.c_uint64 * 7) * 2), ("decode_long_windows", ctypes.c_uint64 * 2),
                 ("decode_combine_launches", ctypes.c_uint64), ("rejected_calls", ctypes.c_uint64),
                 ("insert_decode_launches", ctypes.c_uint64), ("norm_rope_insert_launches", ctypes.c_uint64 * 2),
                 ("norm_rope_insert_decode_launches", ctypes.c_uint64)]
@@ -266,7 +267,9 @@ def get_counters():
     c = Counters()
     _check(lib().fkv_get_counters(ctypes.byref(c)), "fkv_get_counters")
     return {"insert_launches": list(c.insert_launches),
-            "decode_split": [list(r) for r in c.decode_split],
+            "decode_launches": list(c.decode_launches),
+            "decode_row_tiles": [list(r) for r in c.decode_row_tiles],
+            "decode_long_windows": list(c.decode_long_windows),
             "decode_combine_launches": c.decode_combine_launches,
             "insert_decode_launches": c.insert_decode_launches,
             "norm_rope_insert_launches": list(c.norm_rope_insert_launches),

@@ -147,22 +147,16 @@ typedef struct fkv_decode_desc {
   float softmax_scale;         /* > 0, finite; 1/sqrt(128) for these models                 */
   int32_t out_dtype;           /* FKV_OUT_F32 (out is float) or FKV_OUT_BF16 (out is BF16,
                                   each fp32 result rounded to nearest even; the activations
-                                  of the models are BF16: [P1] Contract). BF16 with layouts
-                                  0, 3, 5 and 6 only, else FKV_EUNSUPPORTED               */
+                                  of the models are BF16: [P1] Contract)                   */
   int32_t split_tiles;         /* 0 = automatic; else 32-key tiles per split-KV work group
-                                  (at most 128 with layouts 0, 1, 3, 4, 5 and 6)            */
+                                  (at most 128)                                            */
   int32_t layout;              /* work-group layout: 0 = automatic (layout 5 for an FP8 cache,
                                   except layout 3 for fkv_decode_attn when the packed rows
                                   of a KV head fit one 16-row tile and row_exact is 0;
-                                  layout 3 for a BF16 cache); 1 = query rows spread over
-                                  row groups of at most 32 rows per wave (two waves per SIMD);
-                                  2 = all query rows of a KV head in every wave (one per SIMD);
+                                  layout 3 for a BF16 cache);
                                   3 = row groups of at most 32 rows in separate work groups
-                                  that share K/V tiles through the L2 of one XCD;
-                                  4 = one work group of four waves per split: two halves of
-                                  the query rows x two key lanes, one wave per SIMD, the
-                                  output accumulators in AGPRs (3 to 7 row tiles, else
-                                  FKV_EUNSUPPORTED);
+                                  that share K/V tiles through the L2 of one XCD (16-row
+                                  tiles, MFMA 16x16x32);
                                   5 = 32-row tiles (MFMA 32x32x16), eight waves per work
                                   group, the split's rows in row_groups work groups on one
                                   XCD; splits merged inside the kernel when the grid fits on
@@ -171,7 +165,7 @@ typedef struct fkv_decode_desc {
                                   by each of its four waves (one per SIMD); results bitwise
                                   equal to layout 5 with the same row tiles per work group
                                   (FP8 cache and at least 33 packed rows, else
-                                  FKV_EUNSUPPORTED)                                         */
+                                  FKV_EUNSUPPORTED); any other value: FKV_EINVAL          */
   int32_t row_groups;          /* layout 5: work groups sharing one split's query rows (1, 2
                                   or 4, at most the number of 32-row tiles; 0 = automatic);
                                   layout 6: 0 or the number of 32-row tiles / 2 (else
@@ -321,25 +315,30 @@ int fkv_norm_rope_insert_decode(const fkv_cache* cache, const fkv_decode_desc* d
 const char* fkv_status_string(int status);
 
 /*
- * Runtime execution proof ([P3] "Harness, recovery, and evidence lessons": a
- * runtime entry marker or counter per experimental feature): host-side counts
- * of kernel launches per variant since load or the last reset.
- * decode_split[cache][nt-1] counts split kernels by cache type (0 = FP8,
- * 1 = BF16) and query row tiles nt = ceil((Hq/Hkv)*q_len / 16).
+ * Runtime execution proof ([P3] "Harness, recovery, and evidence lessons": a runtime entry
+ * marker or counter per experimental feature): host-side counts of kernel launches per
+ * variant since load or the last reset. Index 0 is an FP8 cache, 1 a BF16 cache. Every
+ * decode launch (fkv_decode_attn, fkv_insert_decode, fkv_norm_rope_insert_decode) counts once
+ * in decode_launches and once in exactly one of decode_row_tiles (the decode shapes, by
+ * nt = ceil((Hq/Hkv) * q_len / 16) query row tiles, nt <= 7 and q_len <= 16, at index nt - 1)
+ * and decode_long_windows (longer query windows). Counters are updated with relaxed atomics;
+ * only the launching thread's own calls are ordered.
  */
 typedef struct fkv_counters {
-  uint64_t insert_launches[2];      /* [0] FP8, [1] BF16                       */
-  uint64_t decode_split[2][9];
-  uint64_t decode_combine_launches;
-  uint64_t rejected_calls;          /* calls that returned an error            */
-  uint64_t insert_decode_launches;  /* fkv_insert_decode calls (also counted in
-                                       decode_split)                            */
-  uint64_t norm_rope_insert_launches[2];  /* fkv_qk_norm_rope_insert: [0] FP8, [1] BF16 */
-  uint64_t norm_rope_insert_decode_launches;  /* fkv_norm_rope_insert_decode calls (also
-                                                 counted as insert_decode_launches) */
+  uint64_t insert_launches[2];      /* fkv_insert                                               */
+  uint64_t decode_launches[2];      /* decode launches by cache type                            */
+  uint64_t decode_row_tiles[2][7];  /* decode shapes: [cache][nt - 1]                           */
+  uint64_t decode_long_windows[2];  /* query windows beyond 16 tokens or 112 packed rows        */
+  uint64_t decode_combine_launches; /* separate split-combine kernels                           */
+  uint64_t rejected_calls;          /* calls that returned an error                             */
+  uint64_t insert_decode_launches;  /* fkv_insert_decode and fkv_norm_rope_insert_decode calls  */
+  uint64_t norm_rope_insert_launches[2];      /* fkv_qk_norm_rope_insert                        */
+  uint64_t norm_rope_insert_decode_launches;  /* fkv_norm_rope_insert_decode calls              */
 } fkv_counters;
 
+/* Copies the counters into *out. Errors: FKV_EINVAL for a null out. */
 int fkv_get_counters(fkv_counters* out);
+/* Sets every counter to zero. Always FKV_OK. */
 int fkv_reset_counters(void);
 
 #ifdef __cplusplus

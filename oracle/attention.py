@@ -79,24 +79,3 @@ def paged_decode(k_pool, v_pool, q_bits, block_table, seq_lens, q_len, window_le
         q = e4m3.bf16_bits_to_f32(q_bits[b]).astype(np.float64)
         outs.append(decode_attention(q, k, v, q_len, window_left, softmax_scale))
     return np.stack(outs) if outs else np.zeros((0,) + tuple(q_bits.shape[1:]), dtype=np.float64)
-
-
-def decode_attention_heads(q, k, v, q_len, window_left, softmax_scale, heads):
-    """Same as decode_attention but only for the query heads listed (sampled parity at full size)."""
-    q = np.asarray(q, dtype=np.float64)
-    M, Hq, D = q.shape
-    L, Hkv, _ = k.shape
-    G = Hq // Hkv
-    out = {}
-    for h in heads:
-        g = h // G
-        kk = np.asarray(k[:, g, :], dtype=np.float64)
-        vv = np.asarray(v[:, g, :], dtype=np.float64)
-        res = np.empty((M, D))
-        for i in range(M):
-            lo, hi = visible_range(L, M, i, window_left)
-            s = softmax_scale * (kk[lo:hi + 1] @ q[i, h, :])
-            w = np.exp(s - s.max())
-            res[i] = (w @ vv[lo:hi + 1]) / w.sum()
-        out[h] = res
-    return out

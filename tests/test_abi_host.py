@@ -87,7 +87,8 @@ def test_decode_validation_codes():
     bad = [
         (dict(q_len=0), fkv.EINVAL), (dict(q_len=4097), fkv.EUNSUPPORTED), (dict(num_q_heads=17), fkv.EINVAL),
         (dict(q_len=17, layout=3), fkv.EUNSUPPORTED),  # long windows: the 32-row kernel only
-        (dict(num_q_heads=20, q_len=12, layout=1), fkv.EUNSUPPORTED),  # 10 heads per KV head x 12 rows > 112
+        (dict(num_q_heads=20, q_len=12, layout=3), fkv.EUNSUPPORTED),  # 10 heads per KV head x 12 rows > 112
+        (dict(layout=1), fkv.EINVAL), (dict(layout=2), fkv.EINVAL), (dict(layout=4), fkv.EINVAL),  # no such layouts
         (dict(max_seq_len=257), fkv.EINVAL),  # beyond max_blocks_per_seq * block_size
         (dict(max_blocks_per_seq=0), fkv.EINVAL), (dict(num_seqs=-1), fkv.EINVAL),
         (dict(window_left=-2), fkv.EINVAL), (dict(softmax_scale=0.0), fkv.EINVAL),
@@ -101,22 +102,20 @@ def test_decode_validation_codes():
 
 def test_workspace_zero_for_single_split_and_sized_for_many():
     c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
-    one = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256, layout=2)
-    assert one == 0
-    # row-group work groups stage at most 128 page-table entries per split
-    with pytest.raises(fkv.FkvError) as e:
-        _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256, layout=1)
-    assert e.value.status == fkv.EUNSUPPORTED
-    many = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=8)
-    # 32 splits x 8 KV heads x 112 padded rows x (128 + 2) fp32
-    assert many >= 32 * 8 * 112 * 130 * 4
-    # layout 4: two row halves of four 16-row tiles per partial (128 rows), 32 splits per KV
-    # head at 8 KV heads; fewer than three row tiles (q1 at nine heads per KV head) is refused
-    wide = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, layout=4)
-    assert wide == 32 * 8 * 128 * 130 * 4
-    with pytest.raises(fkv.FkvError) as e:
-        _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, q_len=1, layout=4)
-    assert e.value.status == fkv.EUNSUPPORTED
+    for layout in (0, 3, 5):
+        one = _ws(c, num_q_heads=72, max_blocks_per_seq=64, max_seq_len=4096, split_tiles=128, layout=layout)
+        assert one == 0, layout
+    # every work group stages at most 128 page-table entries per split
+    for layout in (3, 5):
+        with pytest.raises(fkv.FkvError) as e:
+            _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=256, layout=layout)
+        assert e.value.status == fkv.EUNSUPPORTED
+    many = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=8, layout=3)
+    # 32 splits x 8 KV heads x 128 padded rows (four row groups of two 16-row tiles) x (128 + 2) fp32
+    assert many == 32 * 8 * 128 * 130 * 4
+    # the 32-row kernel: 128 padded rows per partial, plus 256 bytes of merge counters per pair
+    m32 = _ws(c, num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192, split_tiles=8, layout=5)
+    assert m32 == 32 * 8 * 128 * 130 * 4 + 8 * 256
 
 
 def test_calls_fail_closed_without_touching_the_gpu():
@@ -212,8 +211,8 @@ def test_automatic_q1_workspace_covers_both_kernels():
 
 
 def test_bf16_output_plan_rules():
-    """BF16 output: the row-group and 32-row kernels (layouts 0, 3, 5, 6) write it with the same
-    plan and workspace as fp32; layouts 1, 2 and 4 and unknown output types fail closed."""
+    """BF16 output: every layout (0, 3, 5, 6) writes it with the same plan and workspace as
+    fp32; unknown output types fail closed."""
     c = _fake_cache(num_blocks=4096, bs=64, hkv=8)
     kw = dict(num_q_heads=72, max_blocks_per_seq=128, max_seq_len=8192)
     for layout in (0, 3, 5, 6):
@@ -222,8 +221,7 @@ def test_bf16_output_plan_rules():
                 continue
             assert (_ws(c, layout=layout, q_len=q_len, out_dtype=fkv.OUT_BF16, **kw)
                     == _ws(c, layout=layout, q_len=q_len, **kw)), (layout, q_len)
-    for bad in (dict(layout=1, out_dtype=fkv.OUT_BF16), dict(layout=2, out_dtype=fkv.OUT_BF16),
-                dict(layout=4, out_dtype=fkv.OUT_BF16), dict(out_dtype=0), dict(out_dtype=3)):
+    for bad in (dict(out_dtype=0), dict(out_dtype=3)):
         with pytest.raises(fkv.FkvError) as e:
             _ws(c, **kw, **bad)
         assert e.value.status == fkv.EUNSUPPORTED, bad
@@ -242,7 +240,7 @@ def test_long_query_window_plan_rules():
         ctl = 8 * 256
         parts = (n - ctl) // (rows_pad * 130 * 4)   # fp32 partial rows plus (m, l) per row
         assert n == 0 or (parts >= 1 and n - ctl >= parts * rows_pad * 130 * 4), q_len
-    for bad in (dict(layout=3), dict(layout=6), dict(layout=1), dict(row_groups=2), dict(row_exact=1, split_tiles=8)):
+    for bad in (dict(layout=3), dict(layout=6), dict(row_groups=2), dict(row_exact=1, split_tiles=8)):
         with pytest.raises(fkv.FkvError) as e:
             _ws(c, q_len=64, **kw, **bad)
         assert e.value.status == fkv.EUNSUPPORTED, bad

@@ -1,7 +1,11 @@
-"""GPU parity of fkv_qk_norm_rope_insert against the oracle: the normalised, rotated Q bits
-and every pool byte (K after RMSNorm + RoPE, V as inserted) bit for bit, on the workloads'
-shapes, ragged and padded batches, both page sizes, both cache types and in place; then
-decode attention over the result within the 2e-3 gate."""
+"""GPU parity of fkv_qk_norm_rope_insert against the oracle (the plain float64 RMSNorm and
+rotate-half RoPE, each rounded once to BF16): the normalised, rotated Q bits and the K' pool
+codes bit for bit wherever the float64 value is not within the float32 error band of a
+rounding boundary, and one of the two neighbouring roundings where it is (tests/parity.py,
+norm_rope_bounds); every other pool byte, and V, bit for bit. On the workloads' shapes, ragged
+and padded batches, both page sizes, both cache types and in place; then decode attention
+over the result within the 2e-3 gate, and the in-launch form bitwise equal to the two-launch
+form."""
 
 import dataclasses
 
@@ -56,30 +60,20 @@ def _run(lay, st, inplace=False):
                                                       st.slot_mapping, -1).astype(np.int32))  # past the pool: skipped
     q_ref = normrope.norm_rope_insert(kp, vp, st.q_bits, st.k_bits, st.v_bits, st.q_w, st.k_w, st.eps, st.cos_sin,
                                       st.positions, st.slot_mapping, lay.k_scale, lay.v_scale, lay.block_size,
-                                      lay.num_kv_heads) if lay.cache_dtype == "fp8_e4m3fn" else \
-        _bf16_cache_reference(kp, vp, lay, st)
+                                      lay.num_kv_heads, lay.cache_dtype)
     got_q = q_out.view(torch.int16).cpu().numpy().view(np.uint16)
-    nq = int((got_q != q_ref).sum())
-    assert nq == 0, f"{lay.name}: {nq} Q' elements differ from the oracle"
+    q_lo, q_hi, _ = parity.norm_rope_bounds(st.q_bits, st.q_w, st.eps, st.cos_sin, st.positions)
+    nq_two, nq_diff = parity.check_bf16_within(got_q, q_lo, q_hi, f"{lay.name} Q'")
     dt = np.uint8 if lay.cache_dtype == "fp8_e4m3fn" else np.uint16
     gk = gl.k_pool.cpu().numpy().view(dt)
     gv = gl.v_pool.cpu().numpy().view(dt)
-    assert np.array_equal(gk, kp), f"{lay.name}: {(gk != kp).sum()} K pool elements differ"
     assert np.array_equal(gv, vp), f"{lay.name}: {(gv != vp).sum()} V pool elements differ"
-    print(f"[norm_rope_insert parity] {lay.name}: Q' and pools bit-exact ({st.positions.shape[0]} tokens)",
-          flush=True)
+    k_lo, k_hi, _ = parity.norm_rope_bounds(st.k_bits, st.k_w, st.eps, st.cos_sin, st.positions)
+    nk_two, nk_diff = parity.check_norm_rope_k_pool(gk, kp, lay, st, k_lo, k_hi, lay.name)
+    print(f"[norm_rope_insert parity] {lay.name}: {st.positions.shape[0]} tokens; Q' {got_q.size} elements, "
+          f"{nq_two} near a rounding boundary, {nq_diff} differ from the oracle; K' {nk_two} near, {nk_diff} differ; "
+          f"V and every other pool byte bit-exact", flush=True)
     return gl, q_out, kp, vp, q_ref
-
-
-def _bf16_cache_reference(kp, vp, lay, st):
-    """A BF16 cache stores the rotated K and the raw V bits: the oracle's rotated K through
-    the plain BF16 insert (the oracle's fused step inserts into FP8 pools)."""
-    q_ref = normrope.norm_rope(st.q_bits, st.q_w, st.eps, st.cos_sin, st.positions)
-    k_rot = normrope.norm_rope(st.k_bits, st.k_w, st.eps, st.cos_sin, st.positions)
-    valid = (st.positions >= 0) & (st.positions < st.cos_sin.shape[0])
-    paged.insert(kp, vp, k_rot, st.v_bits, np.where(valid, st.slot_mapping, -1), lay.k_scale, lay.v_scale,
-                 lay.block_size, lay.num_kv_heads, lay.cache_dtype)
-    return q_ref
 
 
 def _cases():
@@ -96,7 +90,7 @@ def _cases():
 
 
 @pytest.mark.parametrize("label,make", list(_cases()), ids=[c[0] for c in _cases()])
-def test_bit_exact_against_the_oracle(label, make):
+def test_against_the_oracle(label, make):
     lay = make()
     _run(lay, synth.norm_rope_step(lay))
 
@@ -197,7 +191,9 @@ def test_norm_rope_inside_the_attention_launch_against_the_oracle():
     q_ref = normrope.norm_rope_insert(kp, vp, st.q_bits, st.k_bits, st.v_bits, st.q_w, st.k_w, st.eps, st.cos_sin,
                                       st.positions, st.slot_mapping, lay.k_scale, lay.v_scale, lay.block_size,
                                       lay.num_kv_heads)
-    assert np.array_equal(gl.k_pool.cpu().numpy(), kp) and np.array_equal(gl.v_pool.cpu().numpy(), vp)
+    assert np.array_equal(gl.v_pool.cpu().numpy(), vp)
+    k_lo, k_hi, _ = parity.norm_rope_bounds(st.k_bits, st.k_w, st.eps, st.cos_sin, st.positions)
+    parity.check_norm_rope_k_pool(gl.k_pool.cpu().numpy(), kp, lay, st, k_lo, k_hi, "c2 in-launch")
     ref = attention.paged_decode(kp, vp, q_ref.reshape(lay.num_seqs, lay.q_len, lay.num_q_heads, 128),
                                  lay.block_table, lay.seq_lens, lay.q_len, lay.window_left, lay.softmax_scale,
                                  lay.k_scale, lay.v_scale, lay.block_size, lay.num_kv_heads, lay.cache_dtype)

@@ -1,8 +1,8 @@
 """GPU parity of long query windows (chunked prefill: q_len new tokens attending causally to
 the cached prefix and to each other) on the 32-row kernel against the oracle, within the
-2e-3 row-normalised gate: windows just past the decode shapes up to 512 tokens, from scratch
-and on long prefixes, global and sliding-window, both page sizes, ragged batches, explicit
-split sizes through the combine kernel, BF16 output."""
+2e-3 row-normalised gate: windows just past the decode shapes up to the 4,096-token maximum,
+from scratch and on long prefixes, global and sliding-window, both page sizes, ragged batches,
+explicit split sizes through the combine kernel, BF16 output."""
 
 import numpy as np
 import pytest
@@ -98,3 +98,53 @@ def test_bf16_output():
     torch.cuda.synchronize()
     assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
     _check(lay, o16, "q64 BF16 output", tol=parity.ATTN_TOL + 2.0 ** -7)
+
+
+def _sampled_rows_check(lay, out, label, kv_heads, rows):
+    """Sampled rows of sequence 0 against the oracle: row i of a q_len-token window equals the
+    one-query attention at seq_len L - q_len + i + 1 (the oracle's own pinned identity), so each
+    sampled row is one oracle call over its visible keys."""
+    M, L = lay.q_len, int(lay.seq_lens[0])
+    G = lay.num_q_heads // lay.num_kv_heads
+    k, v = parity.logical_kv(lay, 0, heads=kv_heads)
+    q = parity.q_f64(lay, 0)
+    gpu = out.float().cpu().numpy()[0]
+    worst = 0.0
+    for i in rows:
+        n = L - M + i + 1
+        for j, g in enumerate(kv_heads):
+            sl = slice(g * G, (g + 1) * G)
+            if n <= 0:
+                assert np.all(gpu[i, sl] == 0.0), (label, i)
+                continue
+            ref = attention.decode_attention(q[i:i + 1, sl], k[:n, j:j + 1], v[:n, j:j + 1], 1, lay.window_left,
+                                             lay.softmax_scale)
+            worst = max(worst, float(parity.row_errors(gpu[i:i + 1, sl], ref).max()))
+    print(f"[prefill parity] {label}: {len(rows)} sampled rows x KV heads {kv_heads}: max row error {worst:.3e}",
+          flush=True)
+    assert worst <= parity.ATTN_TOL, (label, worst)
+
+
+@pytest.mark.parametrize("label,seed,L,q_len,hq,hkv,bs,wl,heads", [
+    ("q2048 from scratch, global, 18/2, p64", 621, 2048, 2048, 18, 2, 64, -1, [0, 1]),
+    ("q2048 on a 2k prefix, window 512, 18/2, p32", 623, 4100, 2048, 18, 2, 32, 511, [1]),
+    ("q4096 maximum on a 2k prefix, global, 72/8, p64", 625, 6144, 4096, 72, 8, 64, -1, [0, 6]),
+], ids=["q2048_scratch", "q2048_window", "q4096_72x8"])
+def test_longest_windows_sampled_rows(label, seed, L, q_len, hq, hkv, bs, wl, heads):
+    """The longest query windows the header allows (up to FKV_MAX_PREFILL_Q_LEN = 4,096 tokens),
+    through the combine kernel, on sampled rows: the first and last rows, rows around tile and
+    window boundaries, and a seeded random sample."""
+    lay = synth.tiny_layer(seed, [L], num_q_heads=hq, num_kv_heads=hkv, block_size=bs, q_len=q_len, window_left=wl)
+    print(f"[prefill parity] {label}: building", flush=True)
+    gl = PagedLayer(lay).build()
+    fkv.reset_counters()
+    out = gl.decode().clone()
+    torch.cuda.synchronize()
+    cnt = fkv.get_counters()
+    assert cnt["decode_long_windows"][0] == 1 and cnt["decode_launches"][0] == 1, cnt
+    assert sum(cnt["decode_row_tiles"][0]) == 0, cnt
+    assert torch.isfinite(out).all()
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, 31, 32, 33, 511, 512, 513, q_len // 2, q_len - 2, q_len - 1}
+    rows |= set(int(r) for r in rng.integers(0, q_len, 24))
+    _sampled_rows_check(lay, out, label, heads, sorted(r for r in rows if r < q_len))

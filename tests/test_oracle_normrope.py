@@ -1,15 +1,17 @@
 """Pins of the oracle's Q/K RMSNorm + RoPE + insert step against things other than itself:
 
-- the library routine torch's float32 -> bfloat16 cast (round to nearest even) for the
-  BF16 rounding;
-- float64 evaluations of the textbook formulas (RMSNorm y = x w / sqrt(mean(x^2) + eps),
-  rotation of the pair (d, d + 64) by the complex factor cos + i sin) within the bound
-  that float32 steps and one BF16 rounding allow;
-- closed forms: a constant vector normalises to its sign times the weight; scaling the
-  input by a power of two leaves the result unchanged when eps = 0; position 0 is the
-  identity; a unit vector in dim d moves into dim d + 64 by the sine of column d;
-- the insert: K' codes decode to the float64 pipeline value within half an E4M3 step,
-  V is inserted exactly as the plain insert does, and padding tokens write nothing.
+- the BF16 rounding: torch's float32 -> bfloat16 cast (round to nearest even) on float32
+  inputs, and an exact brute force with Python fractions on float64 inputs (the nearest BF16
+  value, ties to even, with no intermediate float32 rounding);
+- RMSNorm: the library routine torch.nn.functional.rms_norm in float64;
+- RoPE: multiplication of the complex pair (y_d + i y_(d+64)) by cos + i sin in numpy, and the
+  relative-position property of rotary embeddings;
+- closed forms: a constant vector normalises to its sign times the weight; scaling the input
+  by a power of two leaves the result unchanged when eps = 0; position 0 is the identity; a
+  unit vector in dim d moves into dim d + 64 by the sine of column d;
+- the insert: K' codes decode to the float64 pipeline value within half an E4M3 step plus
+  the BF16 roundings, V is inserted exactly as the plain insert does, and padding tokens
+  write nothing.
 """
 
 import numpy as np
@@ -46,13 +48,59 @@ def test_bf16_rounding_matches_torch():
     assert np.isnan(normrope.bf16_f32(normrope.bf16_bits(np.array([np.nan], np.float32))))[0]
 
 
-def test_sum_of_squares_order_is_within_the_float32_bound():
-    rng = np.random.default_rng(2)
-    x = rng.standard_normal((500, 128)).astype(np.float32) * np.float32(3.0)
-    s32 = normrope.rms_scale(x).astype(np.float64)
-    s64 = (x.astype(np.float64) ** 2).sum(axis=-1)
-    # 7 sequential adds, 4 butterfly adds, 8 rounded products: at most 12 roundings deep
-    assert np.all(np.abs(s32 - s64) <= 12 * EPS24 * s64)
+def _nearest_bf16_fraction(x):
+    """Exact nearest BF16 value of a finite float64 x, ties to even, by brute force over the
+    two BF16 values that bracket it (Python fractions: no rounding anywhere)."""
+    from fractions import Fraction
+    xf = Fraction(float(x))
+    if xf == 0:
+        return 0.0
+    b32 = np.array([x], dtype=np.float32).view(np.uint32)[0]
+    cands = set()
+    for base in (int(b32) >> 16, (int(b32) >> 16) - 1, (int(b32) >> 16) + 1):
+        for sgn in (0, 0x8000):
+            bits = (base & 0x7FFF) | sgn
+            if (bits & 0x7F80) != 0x7F80:
+                cands.add(bits)
+    best = None
+    for bits in cands:
+        v = Fraction(float(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0]))
+        d = abs(v - xf)
+        if best is None or d < best[0] or (d == best[0] and (bits & 1) == 0):
+            best = (d, bits, v)
+    return float(best[2])
+
+
+def test_bf16_rounding_of_float64_values_is_one_rounding():
+    rng = np.random.default_rng(7)
+    xs = list(rng.standard_normal(1500) * 10.0 ** rng.integers(-6, 6, 1500))
+    one = 1.0
+    # just above / below BF16 ties: a float32 intermediate would round these to the tie and
+    # then to even, a single rounding does not
+    xs += [one + 2.0 ** -8 + 2.0 ** -40, one + 2.0 ** -8 - 2.0 ** -40, -(3.0 + 2.0 ** -7 + 2.0 ** -45),
+           one + 3 * 2.0 ** -8 - 2.0 ** -38, 2.0 ** -130 + 2.0 ** -140, 1.5 * 2.0 ** -133]
+    # exact ties: to even
+    xs += [one + 2.0 ** -8, one + 3 * 2.0 ** -8, -(one + 2.0 ** -8)]
+    got = normrope.bf16_round(np.array(xs))
+    want = np.array([_nearest_bf16_fraction(x) for x in xs])
+    assert np.array_equal(got, want)
+    assert normrope.bf16_round(np.array([one + 2.0 ** -8 + 2.0 ** -40]))[0] == one + 2.0 ** -7
+    assert normrope.bf16_round(np.array([one + 2.0 ** -8]))[0] == one
+    # overflow, infinities, signed zero
+    assert np.isinf(normrope.bf16_round(np.array([3.4e38]))).all()
+    assert normrope.bf16_bits(np.array([-0.0]))[0] == 0x8000
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    rng = np.random.default_rng(8)
+    x = _rand_bf16(rng, (300, 4, 128), scale=3.0)
+    w = synth.f32_to_bf16_bits(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    for eps in (1e-6, 1e-2):
+        xt = torch.from_numpy(normrope.bf16_f32(x).astype(np.float64))
+        wt = torch.from_numpy(normrope.bf16_f32(w).astype(np.float64))
+        ref = torch.nn.functional.rms_norm(xt, (128,), wt, eps).numpy()
+        assert np.allclose(normrope.rmsnorm_f64(x, w, eps), ref, rtol=1e-13, atol=0.0)
+        assert np.array_equal(normrope.rmsnorm(x, w, eps), normrope.bf16_bits(ref))
 
 
 @pytest.mark.parametrize("eps,scale", [(1e-6, 5.0), (1e-2, 5.0), (1e-2, 0.05)])  # the last: eps dominates
