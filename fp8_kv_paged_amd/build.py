@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfkv.so")
 OBJ_DIR = os.path.join(HERE, "_build")
-SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip", "fkv_rows.hip", "fkv_m32.hip"]
+SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip", "fkv_rows.hip", "fkv_m32.hip", "fkv_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -351,7 +351,7 @@ struct NormRopeIn {
 static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q, const uint16_t* k_new,
                        const uint16_t* v_new, const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
                        const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-                       const NormRopeIn* nr = nullptr) {
+                       const NormRopeIn* nr = nullptr, const fkv::FixedScratch* fixed = nullptr) {
   const bool fused_insert = k_new != nullptr;
   fkv::DecodePlan p;
   int rc = plan_decode(cache, desc, &p, fused_insert);
@@ -366,8 +366,23 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
     return reject(FKV_EINVAL);
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))) return reject(FKV_EINVAL);
-  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return reject(FKV_EWORKSPACE);
-  if (workspace && !aligned(workspace, 16)) return reject(FKV_EINVAL);
+  char* ctl_base = static_cast<char*>(workspace) + p.ws_ctl_offset;
+  char* part_base = static_cast<char*>(workspace);
+  if (fixed) {
+    // a fixed scratch area: the merge counters at its start (the same place for every call, so
+    // no call's partials can land on another call's counters), the partials after them
+    const uint64_t pairs = (uint64_t)desc->num_seqs * cache->desc.num_kv_heads;
+    if (pairs * 256 > fixed->ctl_bytes || fixed->ctl_bytes + p.ws_o_bytes + p.ws_ml_bytes > fixed->bytes)
+      return reject(FKV_EWORKSPACE);
+    int status = FKV_OK;
+    char* base = static_cast<char*>(fixed->acquire(stream, &status));
+    if (status != FKV_OK || !base) return reject(status != FKV_OK ? status : FKV_EHIP);
+    ctl_base = base;
+    part_base = base + fixed->ctl_bytes;
+  } else {
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return reject(FKV_EWORKSPACE);
+    if (workspace && !aligned(workspace, 16)) return reject(FKV_EINVAL);
+  }
 
   fkv::DecodeArgs a;
   a.k_pool = static_cast<const uint8_t*>(cache->k_pool);
@@ -385,9 +400,9 @@ static int decode_call(const fkv_cache* cache, const fkv_decode_desc* desc, cons
   a.k_w = nr ? nr->k_w : nullptr;
   a.cos_sin = nr ? nr->cos_sin : nullptr;
   a.eps = nr ? nr->eps : 0.f;
-  a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
-  a.ws_ctl = p.ws_ctl_bytes ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.ws_ctl_offset) : nullptr;
+  a.ws_o = p.ws_bytes ? reinterpret_cast<float*>(part_base) : nullptr;
+  a.ws_ml = p.ws_bytes ? reinterpret_cast<float*>(part_base + p.ws_o_bytes) : nullptr;
+  a.ws_ctl = p.ws_ctl_bytes ? reinterpret_cast<uint32_t*>(ctl_base) : nullptr;
   a.fused_combine = p.fused_combine;
   a.xcd_pairs = p.xcd_pairs;
   a.num_seqs = desc->num_seqs;
@@ -432,6 +447,17 @@ int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const u
   return decode_call(cache, desc, q, nullptr, nullptr, block_table, seq_lens, k_scale, v_scale, out, workspace,
                      workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+int fkv::decode_attn_fixed_scratch(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                                   const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                                   const float* v_scale, void* out, const FixedScratch& scratch, void* stream) {
+  return decode_call(cache, desc, q, nullptr, nullptr, block_table, seq_lens, k_scale, v_scale, out, nullptr, 0, stream,
+                     nullptr, &scratch);
+}
+
+extern "C" {
 
 int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q, const uint16_t* k_new,
                       const uint16_t* v_new, const int32_t* block_table, const int32_t* seq_lens,

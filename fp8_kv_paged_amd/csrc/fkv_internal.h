@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/fkv.h"
+
 namespace fkv {
 
 constexpr int kMaxSplits = 512;  // split-KV partials per (sequence, KV head) the combine can merge
@@ -124,6 +126,21 @@ hipError_t launch_rows(const DecodeArgs& a, int ntw, bool fp8, hipStream_t strea
 hipError_t launch_m32(const DecodeArgs& a, int rt, int rw, int kl, bool fp8, hipStream_t stream);
 // Merges split partials (rows_pad rows per partial) into out.
 hipError_t launch_combine(const DecodeArgs& a, bool fp8, hipStream_t stream);
+
+// A scratch area the library owns (fkv_decode_attn_noalloc): `bytes` in all, merge counters in
+// the first `ctl_bytes` (256 per (sequence, KV head) pair; zero before every call, and every
+// call leaves them zero), split partials after them. acquire(stream, &status) returns the
+// area's device address on the current device, setting it up on first use; it runs only
+// after the call's arguments are validated.
+struct FixedScratch {
+  void* (*acquire)(void* stream, int* status);
+  uint64_t bytes;
+  uint64_t ctl_bytes;
+};
+// fkv_decode_attn with its workspace in a FixedScratch (validation, plan and launches shared).
+int decode_attn_fixed_scratch(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                              const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                              const float* v_scale, void* out, const FixedScratch& scratch, void* stream);
 
 // Returns hipErrorInvalidValue when no kernel is compiled for the shape.
 hipError_t launch_decode(const DecodeArgs& a, const SplitShapeInfo& shape, bool fp8, hipStream_t stream,

@@ -1,8 +1,8 @@
 """Python binding of libfkv.so: the C entry points of include/fkv.h, marshalled with ctypes.
 
 Names follow the C ABI without its `fkv_` prefix (cache_bytes, init_cache, insert,
-decode_workspace_bytes, decode_attn, insert_decode, status_string, get_counters,
-reset_counters).
+decode_workspace_bytes, decode_attn, decode_attn_noalloc, insert_decode, qk_norm_rope_insert,
+norm_rope_insert_decode, status_string, get_counters, reset_counters).
 Every step of the path runs in the HIP library; this module only checks tensor
 placement and passes pointers, sizes and the current HIP stream. There is no
 fallback: if the library is missing, loading raises.
@@ -72,6 +72,8 @@ def lib():
         L.fkv_decode_workspace_bytes.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), ctypes.POINTER(sz)]
         L.fkv_decode_attn.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
                                       sz, vp]
+        L.fkv_decode_attn_noalloc.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp,
+                                              vp, vp]
         L.fkv_insert_decode.argtypes = [ctypes.POINTER(Cache), ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, sz, vp]
         L.fkv_qk_norm_rope_insert.argtypes = [ctypes.POINTER(Cache), i32, i32, vp, vp, vp, vp, vp, ctypes.c_float, vp,
@@ -83,7 +85,7 @@ def lib():
         L.fkv_get_counters.argtypes = [ctypes.POINTER(Counters)]
         L.fkv_reset_counters.argtypes = []
         for f in ("fkv_cache_bytes", "fkv_init_cache", "fkv_insert", "fkv_decode_workspace_bytes", "fkv_decode_attn",
-                  "fkv_insert_decode", "fkv_qk_norm_rope_insert", "fkv_norm_rope_insert_decode", "fkv_get_counters", "fkv_reset_counters"):
+                  "fkv_decode_attn_noalloc", "fkv_insert_decode", "fkv_qk_norm_rope_insert", "fkv_norm_rope_insert_decode", "fkv_get_counters", "fkv_reset_counters"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,6 +188,21 @@ def decode_attn(cache, desc, q, block_table, seq_lens, k_scale, v_scale, out, wo
                                  _ptr(k_scale, "k_scale", 4), _ptr(v_scale, "v_scale", 4), _ptr(out, "out", _out_size(desc)), ws,
                                  ws_bytes, _stream(stream)),
            "fkv_decode_attn")
+
+
+def decode_attn_noalloc(cache, desc, q, block_table, seq_lens, k_scale, v_scale, out, stream=None):
+    """fkv_decode_attn_noalloc: decode_attn with the library's static scratch instead of a
+    workspace (nothing is allocated)."""
+    B, M, Hq = desc.num_seqs, desc.q_len, desc.num_q_heads
+    if q.numel() != B * M * Hq * HEAD_DIM or out.numel() != B * M * Hq * HEAD_DIM:
+        raise ValueError("q / out do not match the decode descriptor")
+    if block_table.numel() != B * desc.max_blocks_per_seq or seq_lens.numel() != B:
+        raise ValueError("block_table / seq_lens do not match the decode descriptor")
+    _check(lib().fkv_decode_attn_noalloc(ctypes.byref(cache), ctypes.byref(desc), _ptr(q, "q", 2),
+                                         _ptr(block_table, "block_table", 4), _ptr(seq_lens, "seq_lens", 4),
+                                         _ptr(k_scale, "k_scale", 4), _ptr(v_scale, "v_scale", 4),
+                                         _ptr(out, "out", _out_size(desc)), _stream(stream)),
+           "fkv_decode_attn_noalloc")
 
 
 def insert_decode(cache, desc, q, k_new, v_new, block_table, seq_lens, k_scale, v_scale, out, workspace=None,

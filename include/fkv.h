@@ -10,7 +10,8 @@
  *
  * Conventions shared by every call:
  *  - Every device buffer is owned by the caller. The library allocates no
- *    device memory, keeps no device state and never synchronises the stream.
+ *    device memory and never synchronises the stream; its only device state is
+ *    the static scratch array of fkv_decode_attn_noalloc (loaded with the library).
  *    Fixed-address buffers can therefore be refreshed in place between calls
  *    ([P3] "Result progression": persistent fixed-address attention metadata).
  *  - Pointers named "device" must be device-accessible and 16-byte aligned.
@@ -228,6 +229,30 @@ int fkv_decode_workspace_bytes(const fkv_cache* cache, const fkv_decode_desc* de
 int fkv_decode_attn(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
                     const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
                     const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fkv_decode_attn without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * split-KV scratch (merge counters, then partials) is a static array of the library, one
+ * FKV_NOALLOC_SCRATCH_BYTES copy per GPU it runs on, held until the process ends; the call
+ * itself allocates nothing. Its first call on a device takes the array's device address and,
+ * unless the stream is being captured, clears the counter area on the stream.
+ *
+ *  arguments as fkv_decode_attn, without workspace and workspace_bytes.
+ *
+ * Limits: at most FKV_NOALLOC_MAX_PAIRS (sequence, KV head) pairs, and the plan's partials
+ * (fkv_decode_workspace_bytes less its counters) must fit the array after the counter area
+ * (FKV_NOALLOC_MAX_PAIRS * 256 bytes); beyond either, FKV_EWORKSPACE and nothing is launched.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (other
+ * streams, concurrent graph replays) race and must be serialised by the caller. Outputs are
+ * bitwise those of fkv_decode_attn. Errors: as fkv_decode_attn; FKV_EHIP when the array's
+ * address cannot be obtained.
+ */
+#define FKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define FKV_NOALLOC_MAX_PAIRS 4096
+int fkv_decode_attn_noalloc(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
+                            const int32_t* block_table, const int32_t* seq_lens, const float* k_scale,
+                            const float* v_scale, void* out, void* stream);
 
 /*
  * Cache insertion of the q_len new tokens fused into decode attention: one launch
