@@ -6,15 +6,19 @@ context 8,192 with a 12-token causal verify window (M=12), global attention, pag
 scales) and paged GQA decode attention over the FP8 pages, in one
 fkv_insert_decode launch (split partials merged inside the kernel). The timed steps
 are replayed from one captured HIP graph and checked bit for bit against the eager
-steps; they rotate over enough distinct layer copies (different pools, identical
-contents) that the working set exceeds the 256 MB Infinity Cache, so K/V comes
+steps; every timed step uses its own layer copy (different pools, identical
+contents) and the copies together exceed the 256 MB Infinity Cache, so K/V comes
 from HBM. Insert and decode as two launches are timed beside it.
 
 Prints ONE JSON line. `value` is K/V-read throughput of the whole step
 (algorithmic K/V bytes / step time); `roofline` is that kernel's HBM roofline
 (achieved bandwidth from HIP events on its launch stream, traffic from the
 committed rocprofv3 counter summary when it was taken on this source);
-`cpu_baseline` times the NumPy oracle on host cores.
+`cpu_baseline` times the NumPy oracle on host cores (all threads, and one thread).
+Further keys, each measured in the same run: the 32k-context step, the page-32 vs
+page-64 A/B at 8k and 32k, the 32-sequence batch with FP8 and BF16 caches, the
+attainable read bandwidth of the box (a stream-read probe), and the MFMA busy share
+from the committed counter profile of this source.
 """
 
 import argparse
@@ -34,8 +38,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--context", type=int, default=8192)
     p.add_argument("--block-size", type=int, default=64)
     p.add_argument("--q-len", type=int, default=12)
@@ -45,8 +49,9 @@ def parse():
     p.add_argument("--row-groups", type=int, default=0, help="layout 5: row groups per split (0 = automatic)")
     p.add_argument("--cache-dtype", default="fp8_e4m3fn")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--ab", action="store_true", help="also time the page-size A/B and 32k context")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="seconds of oracle work per thread setting")
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the headline step (no 32k, A/B, batch, probe or CPU sections; for profilers)")
     p.add_argument("--suite", action="store_true",
                    help="also time the other workloads (C1, C2, the C4 cycle eager and as a HIP graph, C5, "
                         "the Q/K norm + RoPE step and a 512-token prefill chunk); no CPU baseline")
@@ -68,7 +73,7 @@ def insert_bytes(q_len, hkv, elem):
     return q_len * hkv * 128 * 2 * (2 + elem)
 
 
-def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
+def run_gpu(args, context, block_size, cache_dtype, steps, warmup, separate=True):
     import torch
     from fp8_kv_paged_amd import fkv, synth
     from fp8_kv_paged_amd.layer import PagedLayer
@@ -78,7 +83,8 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
     base = PagedLayer(lay, split_tiles=args.split_tiles, layout=args.layout, row_groups=args.row_groups).build()
     kv_bytes, other = algorithmic_bytes(context, args.q_len, 72, 8, block_size, 1 if cache_dtype == "fp8_e4m3fn" else 2)
     pool_total = 2 * base.k_pool.numel()
-    copies = args.copies or max(2, math.ceil((1 << 30) / kv_bytes))
+    # each step (warm-up and timed) gets its own copy until the copies hold 1 GiB of K/V
+    copies = args.copies or min(warmup + steps, max(2, math.ceil((1 << 30) / kv_bytes)))
     layers = [base]
     for _ in range(copies - 1):
         c = PagedLayer(lay, poison=False, split_tiles=args.split_tiles, layout=args.layout, row_groups=args.row_groups)
@@ -99,8 +105,9 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
     mean = lambda xs: sum(xs) / len(xs)
     med = lambda xs: sorted(xs)[len(xs) // 2]
     fkv.reset_counters()
-    res = dict(kv_bytes=kv_bytes, other_bytes=other, copies=copies, working_set=copies * kv_bytes,
-               plan_ws=base.workspace.numel(), fused_insert=fused_ok)
+    touched = len({(warmup + i) % copies for i in range(steps)})  # copies the timed steps read
+    res = dict(kv_bytes=kv_bytes, other_bytes=other, copies=copies, copies_timed=touched,
+               working_set=touched * kv_bytes, plan_ws=base.workspace.numel(), fused_insert=fused_ok)
     with torch.cuda.stream(stream):
         # the decode step as one launch: the new tokens' insert fused into the attention call
         if fused_ok:
@@ -148,6 +155,8 @@ def run_gpu(args, context, block_size, cache_dtype, steps, warmup):
             gms, gwall = replay_checked(True)
             res["graph_ms_per_step"] = gms / steps
             res["graph_wall_ms_per_step"] = gwall * 1e3 / steps
+        if not separate:
+            return res
         # the same step as two launches: insert, then decode
         for i in range(warmup):
             L = layers[i % copies]
@@ -357,17 +366,21 @@ def run_suite(iters):
     return out
 
 
-def cpu_baseline(seconds):
-    """The NumPy oracle (as it stands) on the host: insert 12 tokens + paged decode of the
-    same 8k layer, repeated until about `seconds` of CPU work."""
-    import numpy as np
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_steps(seconds):
+    """The NumPy oracle (as it stands) on the host: insert 12 tokens + paged decode of the 8k
+    layer, repeated until about `seconds` of CPU work. Returns (steps, elapsed seconds)."""
     from fp8_kv_paged_amd import synth
     from oracle import attention, paged
-    try:
-        import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     lay = synth.c3_layer(8192, 64)
     kp, vp = paged.new_pools(lay.num_blocks, 64, 8, paged.FP8)
     L = int(lay.seq_lens[0])
@@ -375,19 +388,141 @@ def cpu_baseline(seconds):
     paged.insert(kp, vp, k, v, lay.slots(0, 0, L - 12), lay.k_scale, lay.v_scale, 64, 8, paged.FP8)
     ks, vs = lay.kv_bits(0, L - 12, L)
     sl = lay.slots(0, L - 12, L)
+    q = lay.q_bits()
     n, t0 = 0, time.perf_counter()
     while True:
         paged.insert(kp, vp, ks, vs, sl, lay.k_scale, lay.v_scale, 64, 8, paged.FP8)
-        attention.paged_decode(kp, vp, lay.q_bits(), lay.block_table, lay.seq_lens, 12, -1, lay.softmax_scale,
+        attention.paged_decode(kp, vp, q, lay.block_table, lay.seq_lens, 12, -1, lay.softmax_scale,
                                lay.k_scale, lay.v_scale, 64, 8, paged.FP8)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds:
-            break
+            return n, el
+
+
+def cpu_baseline(seconds):
+    """The oracle timed with the BLAS pool at all its threads, then at one thread (about
+    `seconds` each). `value` is the all-threads figure in the metric's unit (K/V GB/s)."""
+    import threadpoolctl
     kv_bytes = 8192 * 8 * 256
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    n, el = _oracle_steps(seconds)
+    with threadpoolctl.threadpool_limits(limits=1):
+        n1, el1 = _oracle_steps(seconds)
+    sample = "oracle steps (12-token insert + paged decode, 72/8 heads, context 8192, M=12, page 64)"
     return {"value": round(kv_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} oracle steps (12-token insert + paged decode, 72/8 heads, context 8192, M=12, page 64), "
-                      f"{el:.1f} s, {el / n * 1e3:.1f} ms/step"}
+            "sample": f"{n} {sample}, {el:.1f} s, {el / n * 1e3:.1f} ms/step",
+            "us_per_layer": round(el / n * 1e6, 1),
+            "single_thread": {"value": round(kv_bytes * n1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "us_per_layer": round(el1 / n1 * 1e6, 1), "sample": f"{n1} {sample}, {el1:.1f} s"},
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas": [i.get("internal_api") for i in info]}
+
+
+# ---- further sections of the default run ---------------------------------------------------
+
+def device_prefill(gl, seed):
+    """Fills a layer's cache with N(0, 1) BF16 K/V drawn on the GPU (seeded) through fkv_insert,
+    in 32k-token chunks: timing needs the pages' sizes and value distribution, not the host
+    draws the parity tests compare (generating 860k tokens on the host takes minutes)."""
+    import torch
+    from fp8_kv_paged_amd import fkv
+    lay = gl.lay
+    g = torch.Generator(device=gl.device).manual_seed(seed)
+    H = lay.num_kv_heads
+    for b in range(lay.num_seqs):
+        L = int(lay.seq_lens[b])
+        for c0 in range(0, L, 32768):
+            c1 = min(L, c0 + 32768)
+            k = torch.randn((c1 - c0, H, 128), generator=g, device=gl.device).to(torch.bfloat16)
+            v = torch.randn((c1 - c0, H, 128), generator=g, device=gl.device).to(torch.bfloat16)
+            slots = torch.from_numpy(lay.slots(b, c0, c1)).to(gl.device)
+            fkv.insert(gl.cache, k, v, slots, gl.k_scale, gl.v_scale)
+    torch.cuda.synchronize()
+
+
+def run_batch(iters):
+    """The 32-sequence batch (72/8 heads, contexts log-uniform in [1k, 128k], page 32, one shared
+    interleaved pool), FP8 against BF16 caches at M = 12 and M = 1: the automatic kernel of each
+    cache, and the FP8 cache through the BF16 cache's kernel (layout 3: the same code reading
+    half the bytes). Decode calls timed with HIP events (median)."""
+    import torch
+    from fp8_kv_paged_amd import synth
+    from fp8_kv_paged_amd.layer import PagedLayer
+    stream = torch.cuda.Stream()
+    out = {}
+    for dt in ("fp8_e4m3fn", "bf16"):
+        fp8 = dt == "fp8_e4m3fn"
+        base = synth.c5_layer(12, cache_dtype=dt)
+        kv = _visible_kv_bytes(base, 1 if fp8 else 2)
+        gl = PagedLayer(base)
+        device_prefill(gl, 1005)
+        for q_len in (12, 1):
+            lay = synth.c5_layer(q_len, cache_dtype=dt)
+            for layout in ((0, 3) if fp8 else (0,)):
+                g2 = PagedLayer(lay, layout=layout, poison=False) if (q_len, layout) != (12, 0) else gl
+                if g2 is not gl:
+                    g2.k_pool, g2.v_pool, g2.cache = gl.k_pool, gl.v_pool, gl.cache
+                med, _ = _time_calls(lambda: g2.decode(stream), stream, iters, 3)
+                key = f"m{q_len}_{'fp8' if fp8 else 'bf16'}" + ("_layout3" if layout == 3 else "")
+                out[key] = {"decode_us": round(med * 1e3, 2), "kv_bytes": kv,
+                            "kv_gbs": round(kv / (med * 1e-3) / 1e9, 1),
+                            "kv_pct_of_peak": round(100 * kv / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                            "kernel": "decode_rows_kernel (layout 3)" if (layout == 3 or not fp8 or q_len == 1)
+                            else "decode_m32_kernel (layout 5)"}
+                if g2 is not gl:
+                    del g2
+        del gl
+        torch.cuda.empty_cache()
+    for m in (12, 1):
+        f, b16 = out[f"m{m}_fp8_layout3"]["decode_us"], out[f"m{m}_bf16"]["decode_us"]
+        out[f"m{m}_fp8_over_bf16_time_same_kernel"] = round(f / b16, 3)
+        out[f"m{m}_fp8_over_bf16_time_automatic"] = round(out[f"m{m}_fp8"]["decode_us"] / b16, 3)
+    out["workload"] = ("32 sequences, 72 Q / 8 KV heads, contexts log-uniform in [1,024, 131,072] (sum "
+                       f"{int(synth.c5_seq_lens().sum())} tokens), global, page 32; decode only")
+    return out
+
+
+def stream_probe():
+    """Attainable read bandwidth of the box: one pass of the stream-read probe over 16 MiB,
+    64 MiB and 2 GiB buffers (median of 20 passes each; the two small buffers fit in the 256 MB
+    Infinity Cache and are labelled so)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_kv_paged_amd", "libfkv_probe.so"))
+    lib.fkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    stream = torch.cuda.Stream()
+    blocks = 256 * 8
+    sink = torch.empty((blocks,), dtype=torch.int32, device="cuda")
+    out = {}
+    for name, nbytes in (("16MiB_cache_resident", 16 << 20), ("64MiB_cache_resident", 64 << 20), ("2GiB", 2 << 30)):
+        buf = torch.ones((nbytes // 4,), dtype=torch.int32, device="cuda")
+
+        def fn():
+            rc = lib.fkv_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                           blocks, ctypes.c_void_p(stream.cuda_stream))
+            assert rc == 0, rc
+        med, _ = _time_calls(fn, stream, 20, 3)
+        out[name] = {"gbs": round(nbytes / (med * 1e-3) / 1e9, 1), "us": round(med * 1e3, 2)}
+        del buf
+    torch.cuda.empty_cache()
+    out["kernel"] = "stream_read_kernel: 2,048 work groups x 256 threads, 16-byte loads, 4 in flight per thread"
+    return out
+
+
+def counter_profile(src_hash):
+    """MFMA busy share and VALU instructions per MFMA of the decode kernel from the committed
+    rocprofv3 SQ counter summary, when it was taken on this source (else None)."""
+    p = os.path.join(ROOT, "profiles", "decode_sq_counters.json")
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("configs")
 
 
 # split kernel each decode layout launches (layout 0, the automatic choice, is the 32-row kernel for FP8)
@@ -395,9 +530,12 @@ DECODE_KERNELS = {0: "decode_m32_kernel", 3: "decode_rows_kernel", 5: "decode_m3
 
 
 def source_hash():
+    """Hash of the library's kernel and host sources (csrc/*, not the benchmark's probe)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "fp8_kv_paged_amd", "csrc"))):
-        h.update(open(os.path.join(ROOT, "fp8_kv_paged_amd", "csrc", f), "rb").read())
+    d = os.path.join(ROOT, "fp8_kv_paged_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if os.path.isfile(os.path.join(d, f)):
+            h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -473,7 +611,8 @@ def main():
                                f"causal, global, page {args.block_size}, {args.cache_dtype} cache; one step = insert "
                                f"the {args.q_len} new tokens + decode attention",
                    "context": args.context, "q_len": args.q_len, "block_size": args.block_size,
-                   "layer_copies": r["copies"], "working_set_bytes": r["working_set"], "split_tiles": args.split_tiles},
+                   "layer_copies": r["copies"], "layer_copies_timed": r["copies_timed"],
+                   "working_set_bytes": r["working_set"], "split_tiles": args.split_tiles},
         "us_per_layer": round(step_ms * 1e3, 3),
         "step_launches": 1 if r["fused_insert"] else 2,
         "separate_launches": {"step_us": round(r["step_ms"] * 1e3, 3), "insert_us": round(r["insert_ms"] * 1e3, 3),
@@ -494,20 +633,44 @@ def main():
                                "event_us_median": round(r["fused_ms_median"] * 1e3, 3),
                                "wall_us_per_step": round(r["fused_wall_ms_per_step"] * 1e3, 3)}
     line["separate_launches"]["wall_us_per_step"] = round(r["wall_ms_per_step"] * 1e3, 3)
-    if args.ab:
-        extra = {}
-        for ctx, bs in ((8192, 32), (8192, 64), (32768, 32), (32768, 64)):
-            rr = run_gpu(args, ctx, bs, "fp8_e4m3fn", max(20, args.steps // 2), 5)
-            extra[f"{ctx}_p{bs}"] = {"decode_us": round(rr["decode_ms"] * 1e3, 3),
-                                     "decode_kv_gbs": round(rr["kv_bytes"] / (rr["decode_ms"] * 1e-3) / 1e9, 1),
-                                     "insert_us": round(rr["insert_ms"] * 1e3, 3)}
-            if rr["fused_insert"]:
-                extra[f"{ctx}_p{bs}"]["fused_step_us"] = round(rr["fused_ms"] * 1e3, 3)
-        line["ab"] = extra
+    if not args.headline_only:
+        progress = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+        progress("32k step")
+        r32 = run_gpu(args, 32768, args.block_size, args.cache_dtype, args.steps, args.warmup, separate=False)
+        alg32 = r32["kv_bytes"] + r32["other_bytes"] + ins_bytes
+        ms32 = r32["graph_ms_per_step"]
+        line["c3_32k"] = {"us_per_layer": round(ms32 * 1e3, 3),
+                          "kv_gbs": round(r32["kv_bytes"] / (ms32 * 1e-3) / 1e9, 1),
+                          "kv_pct_of_peak": round(100 * r32["kv_bytes"] / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                          "roofline_frac": round(alg32 / (ms32 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "eager_event_us": round(r32["fused_ms"] * 1e3, 3), "layer_copies_timed": r32["copies_timed"],
+                          "working_set_bytes": r32["working_set"],
+                          "workload": "72/8 heads, context 32768, M=12, global, page 64; one graph-replayed "
+                                      "fkv_insert_decode step"}
+        progress("page 32 vs 64")
+        ab = {}
+        for ctx in (8192, 32768):
+            for bs in (32, 64):
+                rr = r if (ctx, bs) == (args.context, args.block_size) else (
+                    r32 if (ctx, bs) == (32768, args.block_size) else
+                    run_gpu(args, ctx, bs, args.cache_dtype, args.steps, args.warmup, separate=False))
+                ms = rr["graph_ms_per_step"]
+                ab[f"{ctx}_p{bs}"] = {"us_per_layer": round(ms * 1e3, 3),
+                                      "kv_gbs": round(rr["kv_bytes"] / (ms * 1e-3) / 1e9, 1)}
+        for ctx in (8192, 32768):
+            ab[f"{ctx}_p32_over_p64_time"] = round(ab[f"{ctx}_p32"]["us_per_layer"] / ab[f"{ctx}_p64"]["us_per_layer"], 3)
+        ab["workload"] = "72/8 heads, M=12, global; graph-replayed fkv_insert_decode steps, same source"
+        line["page_ab"] = ab
+        progress("32-sequence batch, FP8 and BF16 caches")
+        line["batch_fp8_vs_bf16"] = run_batch(max(10, args.steps))
+        progress("stream-read probe")
+        line["attainable_read_bw"] = stream_probe()
+        line["kv_read_pct_of_attainable"] = round(100 * value / line["attainable_read_bw"]["2GiB"]["gbs"], 2)
+        line["counters"] = counter_profile(src)
     if args.suite:
         line["suite"] = run_suite(args.steps)
     # the CPU baseline belongs to the headline line; the suite's line omits it
-    if not args.no_cpu_baseline and not args.suite:
+    if not args.no_cpu_baseline and not args.suite and not args.headline_only:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -1,4 +1,5 @@
-"""Builds libfkv.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree."""
+"""Builds libfkv.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree, and the
+benchmark's stream-read probe (csrc/probe/, libfkv_probe.so: not part of the library)."""
 
 import concurrent.futures
 import os
@@ -8,6 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfkv.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "stream_read.hip")
+PROBE_OUT = os.path.join(HERE, "libfkv_probe.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip", "fkv_rows.hip", "fkv_m32.hip", "fkv_noalloc.hip"]
 
@@ -27,7 +30,7 @@ FLAGS = [
 
 
 def _compile(src):
-    obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(OBJ_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(ln for ln in (r.stderr or "").splitlines() if "packed-fp32-ops" not in ln)
@@ -39,8 +42,9 @@ def _compile(src):
 def build(verbose=False):
     """Compile every source and link libfkv.so. Always recompiles."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(_compile, SOURCES))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        results = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
+    probe_obj = results.pop()[0]
     objs = [o for o, _ in results]
     if verbose:
         for (_, err), src in zip(results, SOURCES):
@@ -52,6 +56,11 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, OUT)
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBE_OUT + ".tmp", probe_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stderr}")
+    os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
     return OUT
 
 

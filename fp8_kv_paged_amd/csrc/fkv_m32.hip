@@ -165,9 +165,14 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t
 // K row fed by A-operand row m of a 32-key tile: bits 2 and 3 of m swapped.
 __device__ __forceinline__ int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// Split partials are written and read with the agent-coherence cache bit (sc1: written
-// through to, and read from, the memory side), so the work groups that merge them need no
-// L2 write-back or invalidate; counters alone order the accesses.
+// Split partials and merge counters are written and read only with the device-scope cache
+// policy (sc1). The LLVM AMDGPU memory model for GFX942/GFX950 (AMDGPUUsage, "Memory Model
+// GFX942") lowers agent-scope monotonic atomic loads, stores and RMWs to exactly these sc1
+// accesses, i.e. they are coherent across the XCDs' separate L2 caches by themselves; its
+// agent-scope release/acquire add an L2 write-back / invalidate only for plain (non-sc1)
+// accesses, plus the vmcnt waits. So the publishing order needs only those waits: every
+// partial store completes (s_waitcnt vmcnt(0), then a barrier) before the finished counter is
+// incremented, and partial loads are issued after the counter load has returned.
 constexpr int kCoherent = 16;  // cache-policy bits of the buffer intrinsics: sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);

@@ -1,0 +1,34 @@
+// Attainable HBM read bandwidth probe for the benchmark (not part of libfkv.so): every byte of
+// a buffer read once with 16-byte vector loads, four per thread in flight, folded with XOR so
+// the loads cannot be dropped, one word per work group written to a sink.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src, uint64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256;
+  uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  u32x4_t acc{0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4_t a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+  __shared__ uint32_t part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+// Reads `bytes` (a multiple of 16, 16-byte aligned) at src with `blocks` work groups of 256
+// threads; sink receives `blocks` words. Returns 0, or 1 for bad arguments, 2 for a launch error.
+extern "C" int fkv_probe_stream_read(const void* src, uint64_t bytes, uint32_t* sink, int blocks, void* stream) {
+  if (!src || !sink || blocks < 1 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15) != 0) return 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4_t*>(src), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}

@@ -4,6 +4,7 @@ reproduces the eager outputs bit for bit, the inserted cache bytes stay those of
 insert, and the launch counters count the captured launches once (at capture) and nothing
 per replay."""
 
+import numpy as np
 import pytest
 import torch
 
@@ -134,3 +135,64 @@ def test_norm_rope_paths_in_a_graph():
         assert all(torch.equal(a, b) for a, b in zip(got, ref)), rep
         assert torch.count_nonzero(one.workspace[nws - ctl:nws]).item() == 0, rep
     print("[graph] norm/RoPE paths: 3 replays equal to eager", flush=True)
+
+
+def test_full_54_layer_cycle_in_one_graph_against_the_oracle():
+    """The whole decode cycle at context 8192 ("Laguna S 2.1 B70 campaign transfer ledger",
+    section "Graph/topology lessons": whole-cycle graph coverage): 36 window-512 layers, 12
+    global layers (each with its own k/v scales) and 6 draft layers at scale 1.0, one
+    fkv_insert_decode launch per layer, captured in ONE HIP graph. Capture records 54 launches,
+    a replay makes none on the host; every replay's output of every layer is within 2e-3 of the
+    oracle and equal to the first replay bit for bit, and every pool equals the oracle's insert
+    of all 8,192 tokens bit for bit."""
+    import parity
+    n = synth.C4_LAYERS + synth.C4_DRAFT_LAYERS
+    lays = [synth.c4_layer(i) for i in range(n)]
+    assert sum(1 for l in lays[:synth.C4_LAYERS] if l.window_left < 0) == 12
+    assert len({(float(l.k_scale), float(l.v_scale)) for l in lays[:synth.C4_LAYERS]}) == 48
+    assert all(l.k_scale == 1.0 and l.v_scale == 1.0 for l in lays[synth.C4_LAYERS:])
+    layers = []
+    for lay in lays:
+        gl = PagedLayer(lay)
+        gl.prefill()          # the 8,180 earlier tokens; the 12 new ones are inserted by the cycle
+        gl.stage_new_tokens()
+        layers.append(gl)
+    torch.cuda.synchronize()
+    print(f"[graph] {n}-layer cycle built", flush=True)
+    stream = torch.cuda.Stream()
+    before = fkv.get_counters()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for gl in layers:
+            gl.insert_decode()
+    torch.cuda.synchronize()
+    mid = fkv.get_counters()
+    assert mid["insert_decode_launches"] - before["insert_decode_launches"] == n
+    assert mid["decode_launches"][0] - before["decode_launches"][0] == n
+    assert mid["decode_combine_launches"] == before["decode_combine_launches"]  # merged inside each kernel
+    first = None
+    for rep in range(3):
+        for gl in layers:
+            gl.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        outs = [gl.out.clone() for gl in layers]
+        if first is None:
+            first = outs
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(outs, first)), rep
+        with torch.cuda.stream(stream):   # eager work between replays
+            layers[rep].decode(stream)
+        stream.synchronize()
+    after = fkv.get_counters()
+    assert after["insert_decode_launches"] == mid["insert_decode_launches"]  # no host launch per replay
+    worst = 0.0
+    for j, (lay, gl) in enumerate(zip(lays, layers)):
+        kp, vp = parity.oracle_pools(lay)
+        assert np.array_equal(gl.k_pool.cpu().numpy(), kp), f"layer {j}: K pool differs from the oracle"
+        assert np.array_equal(gl.v_pool.cpu().numpy(), vp), f"layer {j}: V pool differs from the oracle"
+        err = float(parity.row_errors(first[j].cpu().numpy()[0], parity.reference(lay, 0)).max())
+        assert err <= parity.ATTN_TOL, (j, err)
+        worst = max(worst, err)
+    print(f"[graph] {n}-layer cycle in one graph: 3 replays, pools bit-exact, max row error {worst:.3e}", flush=True)
