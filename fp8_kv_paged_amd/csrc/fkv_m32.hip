@@ -897,11 +897,15 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     ++i;
   }
   for (; i < nsteps; ++i) sync_step(i);  // no tile of this wave left (barriers still counted)
+  // the exchange area below overlays the ring: every wave's last ring read (made after the
+  // last step barrier, possibly by a wave with more tiles than this one) is done before any
+  // wave writes it
+  __syncthreads();
 
   // ---- merge the KL key lanes of each row tile in a fixed order. Every wave writes its
-  // (m, l) and its unscaled accumulators of the groups other key lanes own as soon as its
-  // loop ends; after one barrier each owner rescales and sums its groups over the key lanes
-  // in lane order and stages the merged rows.
+  // (m, l) and its unscaled accumulators of the groups other key lanes own once every wave
+  // has left the loop; after one more barrier each owner rescales and sums its groups over
+  // the key lanes in lane order and stages the merged rows.
   if constexpr (RW == 2) {
     acc_fence32(o[0]);
     acc_fence32(o[1]);
@@ -936,7 +940,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       }
     }
   }
-  __syncthreads();  // also: every ring read is done, the ring area is free
+  __syncthreads();  // every exchange write is done
   const bool direct = (nsplit == 1);
   const float vsc = *a.v_scale;
   const int64_t part = ((int64_t)b * a.num_kv_heads + g) * a.max_splits + s;
