@@ -508,7 +508,8 @@ def stream_probe():
         out[name] = {"gbs": round(nbytes / (med * 1e-3) / 1e9, 1), "us": round(med * 1e3, 2)}
         del buf
     torch.cuda.empty_cache()
-    out["kernel"] = "stream_read_kernel: 2,048 work groups x 256 threads, 16-byte loads, 4 in flight per thread"
+    out["kernel"] = ("stream_read_kernel: 2,048 work groups x 256 threads, one contiguous chunk per work group, "
+                     "16-byte nontemporal loads, 8 in flight per thread")
     return out
 
 
