@@ -737,13 +737,20 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     }
   };
 
+  // ---- the ring's first kDepth - 1 steps are requested before anything else: they need only
+  // the page table
+  const uint32_t slot0 = ring_lane;
+#pragma unroll
+  for (int p = 0; p < S::kDepth - 1; ++p)
+    if (p < nsteps) issue(p);
+
   // ---- fused insert ("Laguna S 2.1 INT4 -- calibrated FP8 KV on Intel B70", section "Initial
   // optimization order": scaled E4M3 insertion; its fusion into the attention call is the
   // next step named there). New token i sits at position L - M + i. The groups whose split
-  // holds new positions encode them into LDS; row group 0 of the split also stores them
-  // into the pool. The ring's copy of a tile holding new keys is patched from LDS after it
-  // is read, so the DMAs need no ordering against the pool stores (whose bytes they may or
-  // may not see).
+  // holds new positions encode them into LDS while the first DMAs are in flight; after the
+  // loop, row group 0 of the split stores them into the pool. The ring's copy of a tile
+  // holding new keys is patched from LDS after it is read, so the DMAs need no ordering
+  // against the pool stores (whose bytes a later call reads).
   __shared__ __align__(16) unsigned char ins_k[16 * kHeadDim];  // [token][dim]
   __shared__ __align__(16) unsigned char ins_v[kHeadDim * 64];  // [dim][position - 32 tn0]
   const int pn0 = max(0, L - M);  // first new position
@@ -753,12 +760,6 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
 #pragma unroll
     for (int u = 0; u < kInsPer; ++u) {
       const int p = L - M + (ci[u] >> 4);  // this chunk's token position
-      // physical block of p from the split's page-table window (lanes hold entries lb0 +
-      // lane and lb0 + 64 + lane); positions outside the split are not stored
-      const int e = min(max((p >> (5 + bshift)) - lb0, 0), 127);
-      const int blo = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_lo);
-      const int bhi = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_hi);
-      const int blk = e < 64 ? blo : bhi;
       if (ins_chunk[u] && p >= 0) {
         uint32_t c0, c1;
         e4m3_encode8(nraw[u], ins_v_chunk[u] ? vs_ins : ks, c0, c1);
@@ -770,23 +771,38 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
           for (int j = 0; j < 8; ++j)
             ins_v[(d0 + j) * 64 + (p - kTile * tn0)] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
         }
-        if (rg == 0 && p >= tb * kTile && p < te * kTile && (unsigned)blk < (unsigned)a.num_blocks) {
-          const int off = p & (a.block_size - 1);
-          const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes;
-          if (!ins_v_chunk[u]) {
-            *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) = u32x2_t{c0, c1};
-          } else {
-            uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + slab + (off >> 3) * 1024 + d0 * 8 + (off & 7);
+      }
+    }
+    // the codes are in LDS before any tile is read
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  // The new tokens' codes into the pool, from LDS; called after the loop's last DMA wait, so
+  // that no store is counted among the DMAs the per-step waits rely on.
+  auto store_new = [&]() {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) vp[j * 8] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
-          }
+    for (int u = 0; u < kInsPer; ++u) {
+      const int p = L - M + (ci[u] >> 4);
+      // physical block of p from the split's page-table window (lanes hold entries lb0 +
+      // lane and lb0 + 64 + lane); positions outside the split are not stored
+      const int e = min(max((p >> (5 + bshift)) - lb0, 0), 127);
+      const int blo = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_lo);
+      const int bhi = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_hi);
+      const int blk = e < 64 ? blo : bhi;
+      if (ins_chunk[u] && p >= 0 && p >= tb * kTile && p < te * kTile && (unsigned)blk < (unsigned)a.num_blocks) {
+        const int d0 = 8 * (ci[u] & 15);
+        const int off = p & (a.block_size - 1);
+        const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes;
+        if (!ins_v_chunk[u]) {
+          *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) =
+              *reinterpret_cast<const u32x2_t*>(ins_k + (ci[u] >> 4) * kHeadDim + d0);
+        } else {
+          uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + slab + (off >> 3) * 1024 + d0 * 8 + (off & 7);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vp[j * 8] = ins_v[(d0 + j) * 64 + (p - kTile * tn0)];
         }
       }
     }
-    // the codes are in LDS before any tile is read; the pool stores stay in flight (they are
-    // older than every DMA, so the per-step DMA waits still count correctly)
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
+  };
   // replaces the ring's bytes of new keys in a tile's registers by their codes
   auto patch = [&](int tile, TileRegs32<true>& x) {
     const int kt = tile * kTile;
@@ -827,10 +843,6 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   // computes S^T of tile i+1 in the same block as the probabilities of tile i, so MFMA and
   // VALU work interleave, then O^T += V^T P^T of tile i.
   const int nfull = wave_rows ? (te - tb - kl + KL - 1) / KL : 0;  // this wave's tiles
-  const uint32_t slot0 = ring_lane;
-#pragma unroll
-  for (int p = 0; p < S::kDepth - 1; ++p)
-    if (p < nsteps) issue(p);
   wait_steps<S::kPerWave, S::kDepth - 2>(min(nsteps - 1, S::kDepth - 2));
   asm volatile("s_barrier" ::: "memory");
   if (S::kDepth - 1 < nsteps) issue(S::kDepth - 1);
@@ -901,6 +913,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   // last step barrier, possibly by a wave with more tiles than this one) is done before any
   // wave writes it
   __syncthreads();
+  if (ins && rg == 0) store_new();
 
   // ---- merge the KL key lanes of each row tile in a fixed order. Every wave writes its
   // (m, l) and its unscaled accumulators of the groups other key lanes own once every wave
