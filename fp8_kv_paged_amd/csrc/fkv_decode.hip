@@ -15,11 +15,12 @@ namespace fkv {
 // Merges the split partials of each (sequence, KV head) row in split order:
 // out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // A thread owns 4 dimensions of one row; a group of 128 threads holds 4 rows. Splits are
-// taken 8 at a time: the 8 partials' (m, l) and output pieces are all requested before
-// any is used (one memory round trip per 8 splits), then folded in split order into a
-// running maximum, row sum and output (the same order for every call).
+// folded 8 at a time, in split order, into a running maximum, row sum and output (the same
+// order for every call); the (m, l) and output pieces of 32 splits are requested before any
+// is used (one memory round trip per 32 splits).
 constexpr int kCombineRows = 4;
 constexpr int kCombineChunk = 8;
+constexpr int kCombineAhead = 4;  // chunks whose loads are in flight together
 
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int kfp8) {
   const int b = blockIdx.z, g = blockIdx.y;
@@ -44,33 +45,44 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a, int k
 
   float mrun = -INFINITY, lrun = 0.f;
   f32x4_t acc{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit; s0 += kCombineChunk) {
-    float ms[kCombineChunk], ls[kCombineChunk];
-    f32x4_t os[kCombineChunk];
+  // kCombineAhead chunks are requested together (one round trip for up to 32 splits), then
+  // folded one chunk at a time as their loads return
+  for (int g0 = 0; g0 < nsplit; g0 += kCombineAhead * kCombineChunk) {
+    float ms[kCombineAhead][kCombineChunk], ls[kCombineAhead][kCombineChunk];
+    f32x4_t os[kCombineAhead][kCombineChunk];
 #pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j) {
-      const int sj = min(s0 + j, nsplit - 1);  // clamped: in-range loads, unused past the end
-      ms[j] = mlp[sj * ml_stride];
-      ls[j] = mlp[sj * ml_stride + a.rows_pad];
-      os[j] = *reinterpret_cast<const f32x4_t*>(op + sj * o_stride);
-    }
-    float mc = mrun;
+    for (int c = 0; c < kCombineAhead; ++c) {
+      if (g0 + c * kCombineChunk >= nsplit) break;  // chunks past the last split are not requested
 #pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j)
-      if (s0 + j < nsplit) mc = fmaxf(mc, ms[j]);
-    // rescale what has been folded so far to the new maximum, then fold this chunk in order
-    const float keep = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mc);
-    lrun *= keep;
-    acc *= keep;
-#pragma unroll
-    for (int j = 0; j < kCombineChunk; ++j) {
-      if (s0 + j < nsplit) {
-        const float wgt = (ms[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[j] - mc);
-        lrun += wgt * ls[j];
-        acc += os[j] * wgt;
+      for (int j = 0; j < kCombineChunk; ++j) {
+        const int sj = min(g0 + c * kCombineChunk + j, nsplit - 1);  // clamped: in-range loads, unused past the end
+        ms[c][j] = mlp[sj * ml_stride];
+        ls[c][j] = mlp[sj * ml_stride + a.rows_pad];
+        os[c][j] = *reinterpret_cast<const f32x4_t*>(op + sj * o_stride);
       }
     }
-    mrun = mc;
+#pragma unroll
+    for (int c = 0; c < kCombineAhead; ++c) {
+      const int s0 = g0 + c * kCombineChunk;
+      if (s0 >= nsplit) break;
+      float mc = mrun;
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j)
+        if (s0 + j < nsplit) mc = fmaxf(mc, ms[c][j]);
+      // rescale what has been folded so far to the new maximum, then fold this chunk in order
+      const float keep = (mrun == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun - mc);
+      lrun *= keep;
+      acc *= keep;
+#pragma unroll
+      for (int j = 0; j < kCombineChunk; ++j) {
+        if (s0 + j < nsplit) {
+          const float wgt = (ms[c][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[c][j] - mc);
+          lrun += wgt * ls[c][j];
+          acc += os[c][j] * wgt;
+        }
+      }
+      mrun = mc;
+    }
   }
   const float vsc = kfp8 ? *a.v_scale : 1.0f;
   const float mul = lrun > 0.f ? vsc / lrun : 0.f;

@@ -881,9 +881,14 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     if (has_new(tile + KL)) patch(tile + KL, xn);
     uint32_t hw[RW][8];
     float lt[RW];
+    // the block of S^T products and probabilities issues at raised wave priority, the P.V
+    // products at the normal one (measured: about 1 % faster steps at 8k and 32k than
+    // without, slower with the priority on the P.V block or alternating between the waves)
+    __builtin_amdgcn_s_setprio(1);
     qk(xn, sn);
 #pragma unroll
     for (int r = 0; r < RW; ++r) lt[r] = probs(sc[r], m_ref[r], hw[r]);
+    __builtin_amdgcn_s_setprio(0);
     finish_tile(xc, hw, lt, sc);
   };
   // the wave's last tile
