@@ -416,7 +416,56 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     if (lb0 + lane < a.max_blocks) bt_lo = btrow[lb0 + lane];
     if (lb0 + lane + 64 < a.max_blocks) bt_hi = btrow[lb0 + lane + 64];
   }
+  // The scales, Q and the new tokens do not depend on the sequence length: they are requested
+  // together with it and the page table, in one round trip.
   int L = a.seq_lens[b];
+  float ks = *a.k_scale;
+  float vs_ins = kIns ? *a.v_scale : 1.0f;
+
+  // ---- this wave's query rows and Q operands: lane (n, hh) of row tile r holds dims
+  // 32j + 16hh .. +15 of row 32 (rtg * RW + r) + n
+  int rl[RW], rpos[RW];
+  u32x4_t qraw[RW][8];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    rl[r] = 32 * (rtg * RW + r) + n;  // row within the work group (LDS index)
+    const int pr = row0 + rl[r];      // packed row of the KV head
+    if (pr < GM) {
+      const int i = pr / G, hq = g * G + (pr - i * G);
+      const u32x4_t* qp =
+          reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qraw[r][2 * j] = qp[4 * j + 2 * hh];
+        qraw[r][2 * j + 1] = qp[4 * j + 2 * hh + 1];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qraw[r][c] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  const bool wave_rows = row0 + 32 * rtg * RW < GM;  // wave-uniform: the wave's row tiles hold a real row
+  // Fused insert: every group requests the q_len new tokens' K and V of its KV head with Q
+  // (thread t < 16 M: K of token t / 16, dims 8 (t % 16) .. +7; the next 16 M threads: V);
+  // only the groups whose split holds the new positions use them.
+  constexpr bool fuse_ins = kIns;  // the instantiation with the new tokens' insert (k_new, v_new set)
+  constexpr int kInsPer = 512 / S::kThreads;  // chunks per thread (32 M <= 512)
+  int ci[kInsPer];
+  bool ins_v_chunk[kInsPer], ins_chunk[kInsPer];
+  u32x4_t nraw[kInsPer];
+#pragma unroll
+  for (int u = 0; u < kInsPer; ++u) {
+    const int t = (int)threadIdx.x + u * S::kThreads;
+    ci[u] = t < 16 * M ? t : t - 16 * M;  // chunk of K or V
+    ins_v_chunk[u] = t >= 16 * M;
+    ins_chunk[u] = fuse_ins && t < 32 * M;
+    nraw[u] = u32x4_t{0u, 0u, 0u, 0u};
+    if (ins_chunk[u]) {
+      const uint16_t* src = (ins_v_chunk[u] ? a.v_new : a.k_new) +
+                            (((int64_t)b * M + (ci[u] >> 4)) * a.num_kv_heads + g) * kHeadDim + 8 * (ci[u] & 15);
+      nraw[u] = *reinterpret_cast<const u32x4_t*>(src);
+    }
+  }
   L = min(L, min(a.max_seq_len, a.max_blocks * a.block_size));
   const int lo_u = (wl < 0) ? 0 : max(0, L - M - wl);
   const int t_first = lo_u / kTile;
@@ -468,54 +517,11 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   }
   const int lo_max = (wl < 0) ? 0 : max(0, L - 1 - wl);  // largest row window start
   const int p_min = L - M;                               // smallest row position
-  float ks = *a.k_scale;
-
-  // ---- this wave's query rows and Q operands: lane (n, hh) of row tile r holds dims
-  // 32j + 16hh .. +15 of row 32 (rtg * RW + r) + n
-  int rl[RW], rpos[RW];
-  u32x4_t qraw[RW][8];
+  // positions of the wave's query rows (-1: padding row)
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
-    rl[r] = 32 * (rtg * RW + r) + n;  // row within the work group (LDS index)
-    const int pr = row0 + rl[r];      // packed row of the KV head
+    const int pr = row0 + rl[r];
     rpos[r] = pr < GM ? L - M + pr / G : -1;
-    if (pr < GM) {
-      const int i = pr / G, hq = g * G + (pr - i * G);
-      const u32x4_t* qp =
-          reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        qraw[r][2 * j] = qp[4 * j + 2 * hh];
-        qraw[r][2 * j + 1] = qp[4 * j + 2 * hh + 1];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qraw[r][c] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  const bool wave_rows = row0 + 32 * rtg * RW < GM;  // wave-uniform: the wave's row tiles hold a real row
-  // Fused insert: every group requests the q_len new tokens' K and V of its KV head with Q
-  // (thread t < 16 M: K of token t / 16, dims 8 (t % 16) .. +7; the next 16 M threads: V);
-  // only the groups whose split holds the new positions use them.
-  constexpr bool fuse_ins = kIns;  // the instantiation with the new tokens' insert (k_new, v_new set)
-  constexpr int kInsPer = 512 / S::kThreads;  // chunks per thread (32 M <= 512)
-  int ci[kInsPer];
-  bool ins_v_chunk[kInsPer], ins_chunk[kInsPer];
-  u32x4_t nraw[kInsPer];
-  float vs_ins = 1.0f;
-#pragma unroll
-  for (int u = 0; u < kInsPer; ++u) {
-    const int t = (int)threadIdx.x + u * S::kThreads;
-    ci[u] = t < 16 * M ? t : t - 16 * M;  // chunk of K or V
-    ins_v_chunk[u] = t >= 16 * M;
-    ins_chunk[u] = fuse_ins && t < 32 * M;
-    nraw[u] = u32x4_t{0u, 0u, 0u, 0u};
-    if (ins_chunk[u]) {
-      const uint16_t* src = (ins_v_chunk[u] ? a.v_new : a.k_new) +
-                            (((int64_t)b * M + (ci[u] >> 4)) * a.num_kv_heads + g) * kHeadDim + 8 * (ci[u] & 15);
-      nraw[u] = *reinterpret_cast<const u32x4_t*>(src);
-      vs_ins = *a.v_scale;
-    }
   }
   // Complete the page-table, Q and new-token loads through an asm that redefines their
   // registers: later reads carry no load dependence, so the compiler adds no wait on the
