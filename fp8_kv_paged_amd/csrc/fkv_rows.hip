@@ -56,7 +56,7 @@ struct RowsShape {
 
 }  // namespace
 
-template <int NTW, int K, bool kFp8>
+template <int NTW, int K, bool kFp8, bool kEarly>
 __global__ __launch_bounds__((RowsShape<NTW, K, kFp8>::kThreads), (K >= 8 ? 2 : 1))
 void decode_rows_kernel(DecodeArgs a) {
   typedef RowsShape<NTW, K, kFp8> S;
@@ -107,6 +107,27 @@ void decode_rows_kernel(DecodeArgs a) {
     if (lb0 + lane < a.max_blocks) bt_lo = btrow[lb0 + lane];
     if (lb0 + lane + 64 < a.max_blocks) bt_hi = btrow[lb0 + lane + 64];
   }
+  // Q does not depend on the sequence length. With kEarly (the grid is about one wave of work
+  // groups) it is requested with the length and the page table, in one round trip; else after
+  // them, so that work groups whose split lies past a short sequence's end request nothing.
+  bf16x8_t qf[NTW][4];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const int r = R0 + 16 * t + n;
+      if (r < GM) {
+        const int i = r / G, h = g * G + (r - i * G);
+        const u32x4_t* qp =
+            reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 32 * q);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qf[t][c] = __builtin_bit_cast(bf16x8_t, qp[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qf[t][c] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
+      }
+    }
+  };
+  if constexpr (kEarly) load_q();
   int L = a.seq_lens[b];
   L = min(L, min(a.max_seq_len, a.max_blocks * a.block_size));
   const int lo_u = (wl < 0) ? 0 : max(0, L - M - wl);
@@ -143,7 +164,6 @@ void decode_rows_kernel(DecodeArgs a) {
   float m_ref[NTW], lsum[NTW];
   int rpos[NTW];
   f32x4_t o[NTW][8];
-  bf16x8_t qf[NTW][4];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int r = R0 + 16 * t + n;
@@ -152,17 +172,8 @@ void decode_rows_kernel(DecodeArgs a) {
     lsum[t] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (r < GM) {
-      const int i = r / G, h = g * G + (r - i * G);
-      const u32x4_t* qp =
-          reinterpret_cast<const u32x4_t*>(a.q + (((int64_t)b * M + i) * a.num_q_heads + h) * kHeadDim + 32 * q);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf[t][c] = __builtin_bit_cast(bf16x8_t, qp[c]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qf[t][c] = __builtin_bit_cast(bf16x8_t, u32x4_t{0u, 0u, 0u, 0u});
-    }
   }
+  if constexpr (!kEarly) load_q();
   // Complete every pending load (page table, Q) here, through an asm that redefines the
   // page-table registers: later reads carry no load dependence, so the compiler adds no
   // wait on the DMAs below, whose counts the loop relies on.
@@ -466,8 +477,14 @@ static hipError_t launch_rows_t(const DecodeArgs& a, hipStream_t stream) {
   // per-XCD pairs: (pairs rounded up to 8) x splits x row groups; else (units rounded up to 8) x row groups
   const int64_t grid = a.xcd_pairs ? ((int64_t)a.num_seqs * a.num_kv_heads + 7) / 8 * 8 * a.max_splits * a.row_groups
                                : (units + 7) / 8 * 8 * a.row_groups;
-  hipLaunchKernelGGL((decode_rows_kernel<NTW, K, kFp8>), dim3((unsigned)grid),
-                     dim3(RowsShape<NTW, K, kFp8>::kThreads), 0, stream, a);
+  // early Q loads pay for a grid of about one wave of work groups (a layer of one sequence),
+  // not for a large batch grid whose work groups mostly leave at once
+  if (grid <= 2 * 256)
+    hipLaunchKernelGGL((decode_rows_kernel<NTW, K, kFp8, true>), dim3((unsigned)grid),
+                       dim3(RowsShape<NTW, K, kFp8>::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_rows_kernel<NTW, K, kFp8, false>), dim3((unsigned)grid),
+                       dim3(RowsShape<NTW, K, kFp8>::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
