@@ -927,10 +927,16 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     ++i;
   }
   for (; i < nsteps; ++i) sync_step(i);  // no tile of this wave left (barriers still counted)
-  // the exchange area below overlays the ring: every wave's last ring read (made after the
-  // last step barrier, possibly by a wave with more tiles than this one) is done before any
-  // wave writes it
-  __syncthreads();
+  // The exchange area and the staged rows below overlay the ring. After the last step barrier
+  // another wave (one with more tiles, or a slower one) may still read the ring slot of the
+  // last step. Where they fit (kWrap), the exchange area takes the ring's other slots, from
+  // the slot after that one on (addresses modulo the ring), and the staged rows follow it,
+  // so a wave writes its exchange data as soon as its loop ends; else a barrier first.
+  constexpr int kStageRow = kHeadDim * 4;  // bytes of a staged row (no padding: swizzled)
+  constexpr bool kWrap = S::kXch <= S::kRing - S::kStepBytes && S::kXch + 32 * RT * kStageRow <= S::kRing &&
+                         (S::kRing & (S::kRing - 1)) == 0;
+  const uint32_t xbase = kWrap ? (uint32_t)((max(nsteps, 1) % S::kDepth) * S::kStepBytes) : 0u;
+  if constexpr (!kWrap) __syncthreads();
   if (ins && rg == 0) store_new();
 
   // ---- merge the KL key lanes of each row tile in a fixed order. Every wave writes its
@@ -946,10 +952,11 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   constexpr int kGpk = 8 / KL;
   // [owner][row tile][source, owner skipped][kGpk*2 quads][64 lanes][4 floats]: 16-byte,
   // lane-contiguous accesses
-  f32x4_t* xch = reinterpret_cast<f32x4_t*>(body);
-  auto xidx = [&](int owner, int rt, int src, int f4) -> int {
+  auto xch = [&](int owner, int rt, int src, int f4) -> f32x4_t& {
     const int slot = src < owner ? src : src - 1;
-    return (((owner * RT + rt) * (KL - 1) + slot) * (kGpk * 2) + f4) * 64 + lane;
+    uint32_t off = (uint32_t)((((owner * RT + rt) * (KL - 1) + slot) * (kGpk * 2) + f4) * 64 + lane) * 16u;
+    if constexpr (kWrap) off = (xbase + off) & (uint32_t)(S::kRing - 1);
+    return *reinterpret_cast<f32x4_t*>(body + off);
   };
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -966,7 +973,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const f32x16_t& acc = o[r][2 * aa + bb];
-        xch[xidx(owner, rtg * RW + r, kl, (gi % kGpk) * 2 + bb)] =
+        xch(owner, rtg * RW + r, kl, (gi % kGpk) * 2 + bb) =
             f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]};
       }
     }
@@ -975,10 +982,20 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
   const bool direct = (nsplit == 1);
   const float vsc = *a.v_scale;
   const int64_t part = ((int64_t)b * a.num_kv_heads + g) * a.max_splits + s;
-  // The merged rows are staged row-major in LDS (rows padded to kStageStride floats:
-  // conflict-free) so that the group's stores write whole contiguous rows.
+  // The merged rows are staged row-major in LDS so that the group's stores write whole
+  // contiguous rows: 4-float column c of row r at c ^ (r % 32) (kWrap: conflict-free without
+  // padding, placed after the exchange area modulo the ring), else at rows padded to
+  // kStageStride floats.
   constexpr int kStageStride = S::kStageStride;
-  float* stage = reinterpret_cast<float*>(body + S::kXch);  // [kRows][kStageStride]
+  auto stage = [&](int row, int col) -> float* {  // col: a multiple of 4
+    if constexpr (kWrap) {
+      const uint32_t c4 = (uint32_t)(col >> 2) ^ (uint32_t)(row & 31);
+      const uint32_t off = (xbase + (uint32_t)S::kXch + (uint32_t)row * kStageRow + c4 * 16u) & (uint32_t)(S::kRing - 1);
+      return reinterpret_cast<float*>(body + off);
+    } else {
+      return reinterpret_cast<float*>(body + S::kXch) + row * kStageStride + col;
+    }
+  };
   __shared__ float sm_row[2 * kRows];                       // merged (M, L) per row
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -1008,15 +1025,14 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
         for (int bb = 0; bb < 2; ++bb) {
           const f32x16_t& acc = o[r][2 * aa + bb];
           const f32x4_t val = (src == kl) ? f32x4_t{acc[4 * ii], acc[4 * ii + 1], acc[4 * ii + 2], acc[4 * ii + 3]}
-                                          : xch[xidx(kl, rtg * RW + r, src, gl * 2 + bb)];
+                                          : xch(kl, rtg * RW + r, src, gl * 2 + bb);
 #pragma unroll
           for (int k = 0; k < 4; ++k) o8[2 * k + bb] += val[k] * ew[src];
         }
       }
       const int d0 = 64 * (gi >> 2) + 16 * (gi & 3) + 8 * hh;
-      float* st = stage + rl[r] * kStageStride + d0;
-      *reinterpret_cast<f32x4_t*>(st) = f32x4_t{o8[0], o8[1], o8[2], o8[3]};
-      *reinterpret_cast<f32x4_t*>(st + 4) = f32x4_t{o8[4], o8[5], o8[6], o8[7]};
+      *reinterpret_cast<f32x4_t*>(stage(rl[r], d0)) = f32x4_t{o8[0], o8[1], o8[2], o8[3]};
+      *reinterpret_cast<f32x4_t*>(stage(rl[r], d0 + 4)) = f32x4_t{o8[4], o8[5], o8[6], o8[7]};
     }
     if (kl == 0 && hh == 0) {
       sm_row[rl[r]] = Mrow;
@@ -1032,7 +1048,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
       const float lw = sm_row[kRows + rr];
       const float mul = lw > 0.f ? vsc / lw : 0.f;
       store_out4(a.out, a.out_bf16, (((int64_t)b * M + i) * a.num_q_heads + hq) * kHeadDim + 4 * d4,
-          *reinterpret_cast<const f32x4_t*>(stage + rr * kStageStride + 4 * d4) * mul);
+          *reinterpret_cast<const f32x4_t*>(stage(rr, 4 * d4)) * mul);
     }
   } else {
     // the partial: rows_pad x 128 fp32 (only the GM real rows written), then (M, L) per row
@@ -1040,7 +1056,7 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
         coherent_rsrc(a.ws_o + part * a.rows_pad * kHeadDim, (uint32_t)(a.rows_pad * kHeadDim * 4));
     for (int idx = threadIdx.x; idx < nrows * (kHeadDim / 4); idx += S::kThreads) {
       const int rr = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage + rr * kStageStride + 4 * d4);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stage(rr, 4 * d4));
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prsrc, (row0 * (kHeadDim / 4) + idx) * 16, 0,
                                              kCoherent);
     }
