@@ -24,7 +24,10 @@ def _pool_bytes(t, cache_dtype):
 def _scales():
     r = np.random.default_rng(77)
     s = list(r.uniform(0.01, 0.1, size=24).astype(np.float32))
-    return s + [np.float32(x) for x in (1.0, 0.5, 2.0 ** -6, 0.0625, 3.0, 1e-3)]
+    # the ends of the reciprocal-correction range, an all-ones significand, and scales outside
+    # that range (IEEE division): tiny, huge, negative
+    edge = (2.0 ** -32, 2.0 ** 32, np.nextafter(np.float32(2.0), np.float32(0.0)), 1e-12, 1e12, -0.05)
+    return s + [np.float32(x) for x in (1.0, 0.5, 2.0 ** -6, 0.0625, 3.0, 1e-3) + edge]
 
 
 def test_every_bf16_pattern_under_many_scales():
