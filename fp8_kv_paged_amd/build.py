@@ -1,5 +1,6 @@
 """Builds libfkv.so (all HIP sources under csrc/) for gfx950 with hipcc, in-tree, and the
-benchmark's stream-read probe (csrc/probe/, libfkv_probe.so: not part of the library)."""
+probe library (csrc/probe/, libfkv_probe.so: not part of the library): the benchmark's
+stream-read probe and the check of the E4M3 conversion helper run by the GPU tests."""
 
 import concurrent.futures
 import os
@@ -9,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libfkv.so")
-PROBE_SRC = os.path.join(CSRC, "probe", "stream_read.hip")
+PROBE_SRCS = [os.path.join(CSRC, "probe", f) for f in ("stream_read.hip", "e4m3_check.hip")]
 PROBE_OUT = os.path.join(HERE, "libfkv_probe.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["fkv_api.hip", "fkv_insert.hip", "fkv_decode.hip", "fkv_rows.hip", "fkv_m32.hip", "fkv_noalloc.hip"]
@@ -42,9 +43,10 @@ def _compile(src):
 def build(verbose=False):
     """Compile every source and link libfkv.so. Always recompiles."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        results = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
-    probe_obj = results.pop()[0]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SRCS)) as ex:
+        results = list(ex.map(_compile, SOURCES + PROBE_SRCS))
+    probe_objs = [o for o, _ in results[len(SOURCES):]]
+    results = results[:len(SOURCES)]
     objs = [o for o, _ in results]
     if verbose:
         for (_, err), src in zip(results, SOURCES):
@@ -56,7 +58,7 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, OUT)
-    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBE_OUT + ".tmp", probe_obj],
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBE_OUT + ".tmp"] + probe_objs,
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"probe link failed:\n{r.stderr}")

@@ -51,20 +51,71 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | (r - (120u << 3));                   // rebias exponent 127 -> 7
 }
 
+// Two fp32 values -> two E4M3FN bytes by the hardware conversion (v_cvt_pk_fp8_f32, round to
+// nearest even), placed in the low (kHigh = false) or high half of old. For every fp32 input
+// with |y| < 448 (NaN excluded) its byte equals e4m3_encode(y): checked on the box over all
+// 2^32 patterns (csrc/probe/e4m3_check.hip, run by the GPU conversion test). It does not
+// saturate like e4m3_encode, and a NaN's code loses its sign, so the callers route such
+// values to e4m3_encode.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3_cvt2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHigh);
+}
+
 // Eight BF16 values (16 bytes; element j in the high or low half of word j/2) -> eight
-// E4M3FN codes: code j = e4m3_encode(fp32(x_j) / scale) with one correctly rounded fp32
-// division, in byte j%4 of lo (j < 4) or hi (j >= 4). Cache insertion, standalone or fused
+// E4M3FN codes: code j = e4m3_encode(fp32(x_j) / scale) with the correctly rounded fp32
+// quotient, in byte j%4 of lo (j < 4) or hi (j >= 4). Cache insertion, standalone or fused
 // into decode, stores exactly these bytes.
+//
+// Quotient. For scales in [2^-32, 2^32] it comes from one reciprocal r = RN(1/scale) and
+// Markstein's residual correction (P. Markstein, "IA-64 and Elementary Functions", 2000):
+// q0 = RN(x r), e = RN(x - q0 scale) (exact, one FMA), q = RN(q0 + e r) (one FMA). With a
+// BF16 dividend (8 significant bits) one correction gives the correctly rounded quotient for
+// every pair of significands (checked exhaustively against IEEE division on the CPU, with
+// every BF16 dividend against scales sampled over the whole range: the host division test).
+// Where that argument does not reach, the codes still agree: for |q0| >= 1024 both quotients
+// saturate (q0 is kept; it may be infinite), and for |x| < 2^-100 the residual may underflow
+// but the quotient lies far below the smallest E4M3 subnormal, so both encode to zero. The
+// sign is x's (scale > 0), NaN included. Other scales (zero, negative, tiny, huge, NaN) take
+// the IEEE division.
+// Code. When all eight quotients have |q| < 448 (an integer test on the magnitude bits, which
+// also catches infinities and NaN) the hardware conversion makes the bytes; else e4m3_encode.
 __device__ __forceinline__ void e4m3_encode8(const u32x4_t& in, float scale, uint32_t& lo, uint32_t& hi) {
-  uint32_t c[2] = {0u, 0u};
+  float x[8], q[8], q0[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t w = in[j >> 1];
-    const float x = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
-    c[j >> 2] |= e4m3_encode(__fdiv_rn(x, scale)) << (8 * (j & 3));
+    x[j] = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
   }
-  lo = c[0];
-  hi = c[1];
+  const bool recip = scale >= 0x1p-32f && scale <= 0x1p32f;
+  if (recip) {
+    const float r = __fdiv_rn(1.0f, scale);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      q0[j] = x[j] * r;
+      q[j] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0[j], scale, x[j]), r, q0[j]), x[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = q0[j] = __fdiv_rn(x[j], scale);
+  }
+  // largest magnitude, as bits shifted past the sign: NaN > infinity > every finite value
+  uint32_t m = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(q[j]) << 1);
+  if (m < (0x43E00000u << 1)) {
+    lo = e4m3_cvt2<true>(q[2], q[3], e4m3_cvt2<false>(q[0], q[1], 0u));
+    hi = e4m3_cvt2<true>(q[6], q[7], e4m3_cvt2<false>(q[4], q[5], 0u));
+  } else {
+    uint32_t c[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float qq = (recip && __builtin_fabsf(q0[j]) >= 1024.0f) ? q0[j] : q[j];
+      c[j >> 2] |= e4m3_encode(qq) << (8 * (j & 3));
+    }
+    lo = c[0];
+    hi = c[1];
+  }
 }
 
 // ---- per-head RMSNorm + rotate-half RoPE in one fixed float32 order ------------------------
