@@ -77,8 +77,7 @@ struct M32Shape {
   static_assert(8 % KL == 0, "output groups split evenly over the key lanes");
   static_assert(RT % RW == 0 && (RW == 1 || RW == 2), "whole row tiles per wave");
   static_assert(kWaves == 4 || kWaves == 8, "one or two waves per SIMD");
-  static constexpr int kInsLds = 16 * kHeadDim + kHeadDim * 64;  // fused insert: K and V codes
-  static_assert(256 + kBody + 2 * KL * RT * 32 * 4 + kInsLds <= 160 * 1024, "LDS budget of one CU");
+  static_assert(256 + kBody + 2 * KL * RT * 32 * 4 <= 160 * 1024, "LDS budget of one CU");
 };
 
 // O^T += V^T P^T. The accumulators stay in VGPRs (MFMA VGPR form): pinning them to AGPRs
@@ -750,120 +749,79 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     }
   };
 
-  // ---- the ring's first kDepth - 1 steps are requested before anything else: they need only
-  // the page table
-  const uint32_t slot0 = ring_lane;
-#pragma unroll
-  for (int p = 0; p < S::kDepth - 1; ++p)
-    if (p < nsteps) issue(p);
-
   // ---- fused insert ("Laguna S 2.1 INT4 -- calibrated FP8 KV on Intel B70", section "Initial
   // optimization order": scaled E4M3 insertion; its fusion into the attention call is the
-  // next step named there). New token i sits at position L - M + i. The groups whose split
-  // holds new positions encode them into LDS while the first DMAs are in flight; after the
-  // loop, row group 0 of the split stores them into the pool. The ring's copy of a tile
-  // holding new keys is patched from LDS after it is read, so the DMAs need no ordering
-  // against the pool stores (whose bytes a later call reads).
-  __shared__ __align__(16) unsigned char ins_k[16 * kHeadDim];  // [token][dim]
-  __shared__ __align__(16) unsigned char ins_v[kHeadDim * 64];  // [dim][position - 32 tn0]
+  // next step named there). New token i sits at position L - M + i. Every group whose key
+  // range holds new positions encodes them and stores their codes into the pool itself (the
+  // row groups of a split store the same bytes), before it requests a ring step holding a
+  // new key: its later DMAs then read the codes from memory like any other key.
+  // Ordering, all within the work group: the stores are issued before the DMAs of those
+  // steps; vector memory operations complete in issue order, so once a wave's wait shows a
+  // DMA issued after its stores complete, the stores are complete too, and the barrier that
+  // follows the wait extends that to every wave of the group (workgroup-scope release and
+  // acquire: the group's waves share one CU and its L1, which the stores write through).
   const int pn0 = max(0, L - M);  // first new position
   const int tn0 = pn0 / kTile;    // first tile holding a new key
   const bool ins = fuse_ins && L > pn0 && pn0 < te * kTile && L > tb * kTile;  // uniform
+  // first step holding a new key; steps from it on are requested after the stores complete
+  const int sn0 = ins ? max(0, tn0 - tb) / KL : S::kDepth;
+  // steps requested before the encode (one, so the encode is not queued behind the others),
+  // and before the first barrier (the rest right after it)
+  const int pre = !ins ? S::kDepth - 1 : (sn0 == 0 ? 0 : 1);
+  const int lim = (!ins || sn0 == 0) ? S::kDepth - 1 : min(sn0, S::kDepth - 1);
+
+  // ---- the ring's first steps are requested before anything else: they need only the
+  // page table
+  const uint32_t slot0 = ring_lane;
+#pragma unroll
+  for (int p = 0; p < S::kDepth - 1; ++p)
+    if (p < pre && p < nsteps) issue(p);
   if (ins) {
 #pragma unroll
     for (int u = 0; u < kInsPer; ++u) {
       const int p = L - M + (ci[u] >> 4);  // this chunk's token position
-      if (ins_chunk[u] && p >= 0) {
-        uint32_t c0, c1;
-        e4m3_encode8(nraw[u], ins_v_chunk[u] ? vs_ins : ks, c0, c1);
-        const int d0 = 8 * (ci[u] & 15);
-        if (!ins_v_chunk[u]) {
-          *reinterpret_cast<u32x2_t*>(ins_k + (ci[u] >> 4) * kHeadDim + d0) = u32x2_t{c0, c1};
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            ins_v[(d0 + j) * 64 + (p - kTile * tn0)] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
-        }
-      }
-    }
-    // the codes are in LDS before any tile is read
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-  // The new tokens' codes into the pool, from LDS; called after the loop's last DMA wait, so
-  // that no store is counted among the DMAs the per-step waits rely on.
-  auto store_new = [&]() {
-#pragma unroll
-    for (int u = 0; u < kInsPer; ++u) {
-      const int p = L - M + (ci[u] >> 4);
       // physical block of p from the split's page-table window (lanes hold entries lb0 +
-      // lane and lb0 + 64 + lane); positions outside the split are not stored
+      // lane and lb0 + 64 + lane); only positions in this group's key range are stored
       const int e = min(max((p >> (5 + bshift)) - lb0, 0), 127);
       const int blo = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_lo);
       const int bhi = __builtin_amdgcn_ds_bpermute((e & 63) * 4, bt_hi);
       const int blk = e < 64 ? blo : bhi;
       if (ins_chunk[u] && p >= 0 && p >= tb * kTile && p < te * kTile && (unsigned)blk < (unsigned)a.num_blocks) {
+        uint32_t c0, c1;
+        e4m3_encode8(nraw[u], ins_v_chunk[u] ? vs_ins : ks, c0, c1);
         const int d0 = 8 * (ci[u] & 15);
         const int off = p & (a.block_size - 1);
         const int64_t slab = ((int64_t)blk * a.num_kv_heads + g) * slab_bytes;
         if (!ins_v_chunk[u]) {
-          *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) =
-              *reinterpret_cast<const u32x2_t*>(ins_k + (ci[u] >> 4) * kHeadDim + d0);
+          *reinterpret_cast<u32x2_t*>(const_cast<uint8_t*>(a.k_pool) + slab + off * kHeadDim + d0) = u32x2_t{c0, c1};
         } else {
           uint8_t* vp = const_cast<uint8_t*>(a.v_pool) + slab + (off >> 3) * 1024 + d0 * 8 + (off & 7);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) vp[j * 8] = ins_v[(d0 + j) * 64 + (p - kTile * tn0)];
+          for (int j = 0; j < 8; ++j) vp[j * 8] = (uint8_t)((j < 4 ? c0 : c1) >> (8 * (j & 3)));
         }
       }
     }
-  };
-  // replaces the ring's bytes of new keys in a tile's registers by their codes
-  auto patch = [&](int tile, TileRegs32<true>& x) {
-    const int kt = tile * kTile;
-    const int pk = kt + key_of_row(n);  // key of this lane's K operand row
-    if (pk >= pn0 && pk < L) {
-      const unsigned char* src = ins_k + (pk - (L - M)) * kHeadDim + 16 * hh;
-      x.k[0][0] = *reinterpret_cast<const u32x4_t*>(src);
-      x.k[0][1] = *reinterpret_cast<const u32x4_t*>(src + 32);
-      x.k[1][0] = *reinterpret_cast<const u32x4_t*>(src + 64);
-      x.k[1][1] = *reinterpret_cast<const u32x4_t*>(src + 96);
-    }
+    // the first step holds a new key: every store completes before any DMA
+    if (sn0 == 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
 #pragma unroll
-    for (int cp = 0; cp < 2; ++cp) {
-      const int k0 = kt + 16 * cp + 8 * hh;  // keys k0 .. k0 + 7 of dims 64 aa + 2n (+1)
-      const int e0 = min(8, max(0, pn0 - k0)), e1 = min(8, max(0, L - k0));
-      if (e0 < e1) {
-        const uint64_t sel = (e1 >= 8 ? ~0ull : ((1ull << (8 * e1)) - 1)) & ~((1ull << (8 * e0)) - 1);
-        const int col = k0 - kTile * tn0;
-#pragma unroll
-        for (int aa = 0; aa < 2; ++aa) {
-          u32x4_t& xv = x.v[2 * cp + aa];
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const uint64_t cw = *reinterpret_cast<const uint64_t*>(ins_v + (64 * aa + 2 * n + bb) * 64 + col);
-            const uint64_t rw = ((uint64_t)xv[2 * bb + 1] << 32) | xv[2 * bb];
-            const uint64_t mw = (rw & ~sel) | (cw & sel);
-            xv[2 * bb] = (uint32_t)mw;
-            xv[2 * bb + 1] = (uint32_t)(mw >> 32);
-          }
-        }
-      }
-    }
-  };
-  auto has_new = [&](int tile) -> bool { return ins && tile * kTile + kTile > pn0 && tile * kTile < L; };
+  for (int p = 0; p < S::kDepth - 1; ++p)
+    if (p >= pre && p < lim && p < nsteps) issue(p);
 
   // ---- the pipeline. kDepth steps are in flight; one barrier per step publishes a step
   // and certifies that every wave has read the slot the next request overwrites. A wave
   // computes S^T of tile i+1 in the same block as the probabilities of tile i, so MFMA and
   // VALU work interleave, then O^T += V^T P^T of tile i.
   const int nfull = wave_rows ? (te - tb - kl + KL - 1) / KL : 0;  // this wave's tiles
-  wait_steps<S::kPerWave, S::kDepth - 2>(min(nsteps - 1, S::kDepth - 2));
+  wait_steps<S::kPerWave, S::kDepth - 2>(min(nsteps - 1, lim - 1));
   asm volatile("s_barrier" ::: "memory");
-  if (S::kDepth - 1 < nsteps) issue(S::kDepth - 1);
+#pragma unroll
+  for (int p = 1; p < S::kDepth; ++p)
+    if (p >= lim && p < nsteps) issue(p);
   TileRegs32<true> xa, xb;
   f32x16_t sa[RW], sb[RW];
   if (nfull > 0) {
     read_slot<true>(slot0, xa);
-    if (has_new(tb + kl)) patch(tb + kl, xa);
     qk(xa, sa);
   }
   // The barrier part of step i (every wave takes part in every step's barrier).
@@ -891,7 +849,6 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
     const int tile = tb + KL * i + kl;
     if (!interior(tile)) mask(tile, sc, xc);
     read_slot<true>(slot0 + (uint32_t)(((i + 1) % S::kDepth) * S::kStepBytes), xn);
-    if (has_new(tile + KL)) patch(tile + KL, xn);
     uint32_t hw[RW][8];
     float lt[RW];
     // the block of S^T products and probabilities issues at raised wave priority, the P.V
@@ -937,7 +894,6 @@ __global__ __launch_bounds__((M32Shape<RT, KL, RW, kFp8>::kThreads), 1) void dec
                          (S::kRing & (S::kRing - 1)) == 0;
   const uint32_t xbase = kWrap ? (uint32_t)((max(nsteps, 1) % S::kDepth) * S::kStepBytes) : 0u;
   if constexpr (!kWrap) __syncthreads();
-  if (ins && rg == 0) store_new();
 
   // ---- merge the KL key lanes of each row tile in a fixed order. Every wave writes its
   // (m, l) and its unscaled accumulators of the groups other key lanes own once every wave

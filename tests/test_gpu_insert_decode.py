@@ -115,6 +115,16 @@ def test_sliding_windows(window_left):
     _fused_vs_separate(lay, f"window {window_left}")
 
 
+@pytest.mark.parametrize("window_left", [-1, 3, 40])
+def test_long_row_windows(window_left):
+    """16 query heads per KV head at q_len 12 (192 packed rows): each row group's key range is
+    clipped to the keys its rows can see, and every row group stores the new tokens inside its
+    own range before it reads them; together they store every new token."""
+    lay = synth.tiny_layer(431 + window_left, [600, 40, 513, 9], num_q_heads=32, num_kv_heads=2, block_size=64,
+                           q_len=12, window_left=window_left)
+    _fused_vs_separate(lay, f"long rows, window {window_left}")
+
+
 def test_row_exact_mode():
     lay = synth.tiny_layer(419, [3000, 257, 12, 5], num_q_heads=18, num_kv_heads=2, block_size=64, q_len=12)
     _fused_vs_separate(lay, "row exact", split_tiles=8, row_exact=1)
