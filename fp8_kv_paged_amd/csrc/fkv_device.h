@@ -96,6 +96,9 @@ __device__ __forceinline__ void e4m3_encode8(const u32x4_t& in, float scale, uin
       q[j] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0[j], scale, x[j]), r, q0[j]), x[j]);
     }
   } else {
+    // a side effect the compiler cannot speculate: without it the eight divisions of this
+    // rare branch are hoisted and computed for every chunk, then discarded by selects
+    asm volatile("");
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[j] = q0[j] = __fdiv_rn(x[j], scale);
   }
