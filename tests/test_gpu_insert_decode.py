@@ -86,13 +86,15 @@ def test_workload_fused_equals_separate(name, make):
     _fused_vs_separate(make(), name)
 
 
-@pytest.mark.parametrize("split_tiles", [0, 1, 2])
+@pytest.mark.parametrize("split_tiles", [0, 1, 2, 8, 12])
 @pytest.mark.parametrize("block_size", [32, 64])
 def test_ragged_boundaries(block_size, split_tiles):
     """New positions straddling 32-key tiles, pages and (split_tiles 1, 2) splits; sequences
-    shorter than q_len (positions below 0 are not stored)."""
-    lay = synth.tiny_layer(401 + block_size, [40, 70, 64, 129, 700, 12, 5, 1], num_q_heads=18, num_kv_heads=2,
-                           block_size=block_size, q_len=12, pool_slack=2.0, outlier_rate=0.01)
+    shorter than q_len (positions below 0 are not stored). With 8 and 12 tiles per split the
+    new keys fall in the first, second or third ring step of their split (the stores must
+    complete before that step is requested)."""
+    lay = synth.tiny_layer(401 + block_size, [40, 70, 64, 129, 700, 12, 5, 1, 300, 1000], num_q_heads=18,
+                           num_kv_heads=2, block_size=block_size, q_len=12, pool_slack=2.0, outlier_rate=0.01)
     _fused_vs_separate(lay, f"ragged p{block_size} split_tiles {split_tiles}", split_tiles=split_tiles)
 
 
