@@ -94,10 +94,12 @@ typedef struct fkv_cache {
 int fkv_cache_bytes(const fkv_cache_desc* desc, size_t* k_bytes, size_t* v_bytes);
 
 /*
- * Fills *out from desc and two caller-owned device pools of fkv_cache_bytes each.
- * No allocation and no device work: pool contents stay undefined until tokens
- * are inserted. Errors as fkv_cache_bytes, plus FKV_EINVAL for null or
- * misaligned pools.
+ * Fills *out from desc and two caller-owned device pools of fkv_cache_bytes each
+ * (the paged E4M3 K and V pools of [P1] Contract and [P2] "Page-32 attention
+ * experiment"; the pools stay the caller's, as the fixed-address buffers of
+ * [P3] "Result progression"). No allocation and no device work: pool contents
+ * stay undefined until tokens are inserted. Errors as fkv_cache_bytes, plus
+ * FKV_EINVAL for null or misaligned pools.
  */
 int fkv_init_cache(const fkv_cache_desc* desc, void* k_pool, void* v_pool, fkv_cache* out);
 
@@ -184,8 +186,9 @@ typedef struct fkv_decode_desc {
 
 /*
  * Bytes of device workspace fkv_decode_attn needs for (cache, desc): split-KV
- * partial results and, for layout 5, 256 bytes of merge counters per (sequence,
- * KV head) at its end. With the automatic layout and one 16-row tile of an FP8
+ * partial results (the long-context decode of [P4] "BF16 versus FP8 in concrete
+ * terms" is split along the keys to fill the chip) and, for layout 5, 256 bytes
+ * of merge counters per (sequence, KV head) at its end. With the automatic layout and one 16-row tile of an FP8
  * cache the size covers both kernels that fkv_decode_attn and fkv_insert_decode
  * then run, so one workspace serves both calls. Pure host arithmetic; may be 0. The workspace must be
  * zero-filled once before its first use (the counters must start at zero); every
@@ -336,7 +339,9 @@ int fkv_norm_rope_insert_decode(const fkv_cache* cache, const fkv_decode_desc* d
                                 const float* v_scale, void* out, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
-/* Human-readable text of a status code (static storage). */
+/* Human-readable text of a status code (static storage). Bookkeeping: no passage of
+ * the pages defines it; it names the FKV_E* refusals, which replace any fallback
+ * ([P2] "Transferable learnings"). */
 const char* fkv_status_string(int status);
 
 /*
