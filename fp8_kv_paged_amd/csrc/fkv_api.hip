@@ -152,10 +152,15 @@ int plan_layout(const fkv_cache* c, const fkv_decode_desc* d, int layout, fkv::D
     const int kl = (sh.groups_per_cu == -3 || d->row_exact) ? 4 : 8 / (rt_total / rg);
     p->key_lanes = kl;
     if (tps == 0) {
-      // Fill the chip, but with at most kFastMergeSplits splits: with few (sequence, KV head)
-      // pairs more splits of one step each cost more in partials and merging than they gain
-      // (measured at 18/2 heads, 8k: 64 one-step splits 29.6 us, 16 four-step splits 20.3 us).
-      const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / (bg * rg), fkv::kFastMergeSplits));
+      // Fill the chip, but with at most kFastMergeSplits splits, or up to twice that while
+      // every split keeps at least four steps of kl tiles: with few (sequence, KV head) pairs
+      // more splits of one step each cost more in partials and merging than they gain
+      // (measured at 18/2 heads, 8k: 64 one-step splits 29.6 us, 16 four-step splits
+      // 20.3 us), while 32 four-step splits beat 16 eight-step ones with the layer in HBM
+      // (72/8 heads, q1, 32k: 29.8 vs 31.8-33.1 us per graph-replayed fused step).
+      const int64_t cap = std::max<int64_t>(fkv::kFastMergeSplits,
+                                            std::min<int64_t>(2 * fkv::kFastMergeSplits, tiles_max / (4 * kl)));
+      const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(kNumCUs / (bg * rg), cap));
       tps = (tiles_max + splits - 1) / splits;
       tps = (tps + kl - 1) / kl * kl;
       tps = std::min<int64_t>(tps, fkv::kMaxDmaSplitTiles);
