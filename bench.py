@@ -16,7 +16,8 @@ Prints ONE JSON line. `value` is K/V-read throughput of the whole step
 committed rocprofv3 counter summary when it was taken on this source);
 `cpu_baseline` times the NumPy oracle on host cores (all threads, and one thread).
 Further keys, each measured in the same run: the 32k-context step, the page-32 vs
-page-64 A/B at 8k and 32k, the 32-sequence batch with FP8 and BF16 caches, the
+page-64 A/B at 8k and 32k, the q1 fused step at 8k and 32k, the 32-sequence batch
+with FP8 and BF16 caches, the
 attainable read bandwidth of the box (a stream-read probe), and the MFMA busy share
 from the committed counter profile of this source.
 """
@@ -684,6 +685,17 @@ def main():
             ab[f"{ctx}_p32_over_p64_time"] = round(ab[f"{ctx}_p32"]["us_per_layer"] / ab[f"{ctx}_p64"]["us_per_layer"], 3)
         ab["workload"] = "72/8 heads, M=12, global; graph-replayed fkv_insert_decode steps, same source"
         line["page_ab"] = ab
+        progress("q1 steps")
+        a1 = argparse.Namespace(**{**vars(args), "q_len": 1})
+        q1 = {}
+        for ctx in (8192, 32768):
+            rq = run_gpu(a1, ctx, args.block_size, args.cache_dtype, args.steps, args.warmup, separate=False)
+            ms = rq["graph_ms_per_step"]
+            q1[str(ctx)] = {"us_per_layer": round(ms * 1e3, 3),
+                            "kv_gbs": round(rq["kv_bytes"] / (ms * 1e-3) / 1e9, 1),
+                            "hot_mall_resident_us": round(rq["hot_graph_ms_per_step"] * 1e3, 3)}
+        q1["workload"] = "72/8 heads, q_len 1, global, page 64; graph-replayed fkv_insert_decode steps"
+        line["q1_steps"] = q1
         progress("32-sequence batch, FP8 and BF16 caches")
         line["batch_fp8_vs_bf16"] = run_batch(max(10, args.steps))
         progress("stream-read probe")
