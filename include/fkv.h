@@ -271,9 +271,11 @@ int fkv_decode_attn_noalloc(const fkv_cache* cache, const fkv_decode_desc* desc,
  *  other arguments as fkv_decode_attn (same descriptor, workspace and rules).
  *
  * The pool bytes written are those fkv_insert writes for the same tokens, and out is
- * bitwise equal to fkv_decode_attn's after that insert. The attention reads the new
- * keys from the codes it computed, not back from the pool, so no ordering between
- * the two is needed. FP8 cache and layout 0, 5 or 6 only (else FKV_EUNSUPPORTED).
+ * bitwise equal to fkv_decode_attn's after that insert. Each work group encodes the new
+ * tokens of its own key range, stores the codes into the pool and waits for those stores
+ * to complete before it reads those keys back (work groups that share a key range store
+ * the same bytes). Other work must not read or write the receiving pool blocks during
+ * the call. FP8 cache and layout 0, 5 or 6 only (else FKV_EUNSUPPORTED).
  * Errors: as fkv_decode_attn, plus FKV_EINVAL for a null or misaligned k_new/v_new.
  */
 int fkv_insert_decode(const fkv_cache* cache, const fkv_decode_desc* desc, const uint16_t* q,
