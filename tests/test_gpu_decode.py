@@ -122,6 +122,8 @@ EDGE = [
     ([257, 1000], 7, -1, 16, 1, 64, "fp8_e4m3fn"),
     ([100], 3, 17, 12, 4, 32, "fp8_e4m3fn"),
     ([5000], 12, -1, 9, 1, 32, "fp8_e4m3fn"),
+    ([16, 40, 300], 16, -1, 14, 2, 32, "fp8_e4m3fn"),  # q_len at its maximum, 112 packed rows
+    ([16, 900], 16, 100, 4, 4, 64, "fp8_e4m3fn"),      # q_len 16 of one head per KV head: one 16-row tile
     ([12, 77, 300], 12, 64, 18, 2, 32, "bf16"),
     ([1, 33, 129], 1, -1, 18, 2, 64, "bf16"),
 ]

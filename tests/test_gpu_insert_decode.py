@@ -151,6 +151,16 @@ def test_q1_decode_and_fused_share_one_workspace():
         _check(lay, out_d, f"q1 decode {rep}")
 
 
+@pytest.mark.parametrize("hq,hkv,block_size", [(14, 2, 32), (4, 4, 64)])
+def test_max_query_length(hq, hkv, block_size):
+    """q_len 16, the largest the fused call stages: every thread of the group holds a new-token
+    chunk (112 packed rows at 7 heads per KV head; one 16-row tile at one head), with
+    sequences shorter than, equal to and longer than q_len."""
+    lay = synth.tiny_layer(431 + hq, [16, 9, 40, 700], num_q_heads=hq, num_kv_heads=hkv, block_size=block_size,
+                           q_len=16, pool_slack=2.0, outlier_rate=0.01)
+    _fused_vs_separate(lay, f"q_len 16, {hq}/{hkv} heads, page {block_size}")
+
+
 def test_single_query():
     lay = synth.tiny_layer(413, [1, 32, 33, 300], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=1)
     _fused_vs_separate(lay, "q1")

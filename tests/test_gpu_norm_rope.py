@@ -139,6 +139,8 @@ def _fused_cases():
     yield "q1 batch of 24, 72/8", lambda: synth.tiny_layer(523, list(range(1, 1200, 50)), num_q_heads=72,
                                                             num_kv_heads=8, block_size=64, q_len=1), {}
     yield "c3 8k page 64, layout 6", lambda: synth.c3_layer(8192, 64), {"layout": 6}
+    yield "q_len 16, 14/2", lambda: synth.tiny_layer(525, [16, 9, 500], num_q_heads=14, num_kv_heads=2,
+                                                      block_size=32, q_len=16), {}
 
 
 @pytest.mark.parametrize("label,make,kw", list(_fused_cases()), ids=[c[0] for c in _fused_cases()])
