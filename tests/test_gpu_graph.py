@@ -4,6 +4,8 @@ reproduces the eager outputs bit for bit, the inserted cache bytes stay those of
 insert, and the launch counters count the captured launches once (at capture) and nothing
 per replay."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -86,6 +88,60 @@ def test_decode_graph_with_split_merge_counters():
         torch.cuda.synchronize()
         assert torch.equal(gl.out, ref), rep
         assert torch.count_nonzero(gl.workspace[nws - ctl:nws]).item() == 0, rep
+
+
+def test_fused_steps_replayed_with_metadata_refreshed_in_place():
+    """Three decode steps of one layer from a single captured fkv_insert_decode: before each replay
+    the sequence lengths and the new tokens are rewritten in place in the captured buffers (the
+    block table already holds the final capacity, the descriptor's max_seq_len the final length).
+    Every replay equals the eager fused call of the same step bit for bit (pools and output) and
+    the oracle, and launches nothing from the host."""
+    final = synth.tiny_layer(661, [524, 114, 3000], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=12,
+                             pool_slack=2.0)
+    graphed, eager = PagedLayer(final), PagedLayer(final)
+    for gl in (graphed, eager):
+        for b in range(final.num_seqs):
+            gl.insert_tokens(b, 0, int(final.seq_lens[b]) - 36)
+
+    def at_step(step):
+        return dataclasses.replace(final, seq_lens=(final.seq_lens - 12 * (2 - step)).astype(np.int32))
+
+    def refresh(gl, lay):
+        gl.lay = lay
+        gl.seq_lens.copy_(torch.from_numpy(lay.seq_lens))
+        k, v = gl.new_k, gl.new_v
+        gl.stage_new_tokens()
+        if k is not None:  # keep the captured buffers, rewrite their contents
+            k.copy_(gl.new_k)
+            v.copy_(gl.new_v)
+            gl.new_k, gl.new_v = k, v
+
+    import parity
+
+    refresh(graphed, at_step(0))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        graphed.insert_decode()
+    torch.cuda.synchronize()
+    for step in range(3):
+        lay = at_step(step)
+        refresh(graphed, lay)
+        torch.cuda.synchronize()
+        before = fkv.get_counters()["insert_decode_launches"]
+        g.replay()
+        torch.cuda.synchronize()
+        assert fkv.get_counters()["insert_decode_launches"] == before, step  # no host launch
+        refresh(eager, lay)
+        out_e = eager.insert_decode().clone()
+        torch.cuda.synchronize()
+        assert torch.equal(graphed.k_pool, eager.k_pool) and torch.equal(graphed.v_pool, eager.v_pool), step
+        assert torch.equal(graphed.out, out_e), step
+        gpu = graphed.out.cpu().numpy()
+        worst = max(float(parity.row_errors(gpu[b], parity.reference(lay, b)).max()) for b in range(lay.num_seqs))
+        print(f"[graph] fused step {step} replayed with refreshed metadata: max row error {worst:.3e}", flush=True)
+        assert worst <= parity.ATTN_TOL, (step, worst)
 
 
 def test_norm_rope_paths_in_a_graph():
