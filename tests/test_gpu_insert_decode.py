@@ -161,6 +161,37 @@ def test_max_query_length(hq, hkv, block_size):
     _fused_vs_separate(lay, f"q_len 16, {hq}/{hkv} heads, page {block_size}")
 
 
+def _random_case(seed):
+    """A seeded random shape: 1-8 KV heads, 1-16 query heads per KV head, 1-16 new tokens,
+    page 32 or 64, global or a random window, 1-12 sequences up to 3k or 9k tokens (some
+    shorter than q_len), automatic layout, layout 5 or (with 33-112 packed rows) layout 6, and
+    an automatic or fixed split size."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.integers(1, 17))
+    M = int(rng.integers(1, 17))
+    bs = int(rng.choice([32, 64]))
+    wl = -1 if rng.random() < 0.5 else int(rng.integers(0, 700))
+    ns = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(0, int(rng.choice([3000, 9000])), ns)]
+    if rng.random() < 0.3:
+        lens[0] = int(rng.integers(0, M + 1))
+    layout = int(rng.choice([0, 5, 6]))
+    st = int(rng.choice([0, 0, 1, 2, 4, 8, 12, 16]))
+    if layout == 6 and not 32 < G * M <= 112:
+        layout = 5
+    lay = synth.tiny_layer(9000 + seed, lens, num_q_heads=G * hkv, num_kv_heads=hkv, block_size=bs, q_len=M,
+                           window_left=wl, pool_slack=2.0)
+    return lay, dict(layout=layout, split_tiles=st)
+
+
+@pytest.mark.parametrize("seed", range(200, 212))
+def test_random_shapes(seed):
+    lay, kw = _random_case(seed)
+    _fused_vs_separate(lay, f"random shape {seed} ({lay.num_q_heads}/{lay.num_kv_heads} heads, q_len {lay.q_len}, "
+                            f"page {lay.block_size}, window {lay.window_left}, {kw})", **kw)
+
+
 def test_single_query():
     lay = synth.tiny_layer(413, [1, 32, 33, 300], num_q_heads=18, num_kv_heads=2, block_size=32, q_len=1)
     _fused_vs_separate(lay, "q1")
