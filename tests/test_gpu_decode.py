@@ -129,6 +129,57 @@ EDGE = [
 ]
 
 
+def _random_decode_case(seed):
+    """A seeded random shape: 1-8 KV heads, 1-16 query heads per KV head, 1-16 query tokens
+    (sometimes 17-64: a long window), page 32 or 64, global or a random window, 1-8 sequences up
+    to 3k or 9k tokens, an FP8 or (a quarter of the cases) BF16 cache, layout 0, 3, 5 or 6, and an
+    automatic or fixed split size."""
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.integers(1, 17))
+    M = int(rng.integers(1, 17)) if rng.random() < 0.85 else int(rng.integers(17, 65))
+    bs = int(rng.choice([32, 64]))
+    wl = -1 if rng.random() < 0.5 else int(rng.integers(0, 700))
+    ns = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(M, int(rng.choice([3000, 9000])), ns)]
+    dt = "bf16" if rng.random() < 0.25 else "fp8_e4m3fn"
+    layout = int(rng.choice([0, 3, 5, 6]))
+    st = int(rng.choice([0, 0, 1, 2, 4, 8, 12, 16]))
+    lay = synth.tiny_layer(7000 + seed, lens, num_q_heads=G * hkv, num_kv_heads=hkv, block_size=bs, q_len=M,
+                           window_left=wl, cache_dtype=dt, pool_slack=2.0)
+    return lay, dict(layout=layout, split_tiles=st)
+
+
+def _supported(lay, layout):
+    """The documented shape rules: long windows (more than 16 query tokens or 112 packed rows)
+    on FP8 caches with layout 0 or 5 only; layouts 5 and 6 read FP8 caches; layout 6 needs 33 to
+    112 packed rows; layout 3 at most 112."""
+    rows = lay.num_q_heads // lay.num_kv_heads * lay.q_len
+    fp8 = lay.cache_dtype == "fp8_e4m3fn"
+    long_rows = rows > 112 or lay.q_len > 16
+    if long_rows:
+        return fp8 and layout in (0, 5)
+    if layout in (5, 6) and not fp8:
+        return False
+    return not (layout == 6 and rows <= 32)
+
+
+@pytest.mark.parametrize("seed", range(300, 314))
+def test_random_decode_shapes(seed):
+    lay, kw = _random_decode_case(seed)
+    label = (f"random decode {seed} ({lay.num_q_heads}/{lay.num_kv_heads} heads, q_len {lay.q_len}, page "
+             f"{lay.block_size}, window {lay.window_left}, {lay.cache_dtype}, {kw})")
+    if not _supported(lay, kw["layout"]):
+        with pytest.raises(fkv.FkvError) as e:
+            PagedLayer(lay, **kw)
+        assert e.value.status == fkv.EUNSUPPORTED, label
+        return
+    gl = PagedLayer(lay, **kw).build()
+    out = gl.decode().clone()
+    torch.cuda.synchronize()
+    _check(lay, out, label=label)
+
+
 @pytest.mark.parametrize("layout", [3, 5])
 @pytest.mark.parametrize("case", EDGE, ids=[f"L{c[0]}-M{c[1]}-w{c[2]}-{c[3]}x{c[4]}-p{c[5]}-{c[6][:4]}" for c in EDGE])
 def test_edge_cases(case, layout):
